@@ -1,0 +1,213 @@
+/*
+ * gdn.h -- C ABI of libgdn: the Gated DeltaNet layer core on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (the oxydllm 0.0.0-alpha.12.2 release notes, "New Features",
+ * Gated DeltaNet runtime) keeps, per sequence and v-head, a d_k x d_v fp32
+ * memory S and for every token t does
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,          alpha_t = exp(g_t),
+ *
+ * (S stored [d_k][d_v]; this is the usual d_v x d_k formulation transposed).
+ * Prefill runs it as a chunked parallel scan, decode as an O(1) recurrent
+ * step; a short causal depthwise convolution (+SiLU) produces q, k, v from
+ * the projected activations (Vallmo.jl README, "What's here": causal conv1d
+ * and the fused/recurrent DeltaNet paths are the hybrid layer's kernels).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers, allocated and owned by the
+ *    caller.  The library never allocates device memory; scratch space is
+ *    the caller's `workspace` (size from gdn_prefill_workspace_size).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  It returns once the work is queued.  Host-side
+ *    validation happens first: a call that returns an error other than
+ *    GDN_ERR_HIP has queued nothing and touched no memory.
+ *  - Layouts are token-major and row-major:
+ *      q, k   [N_tok][H_k][d_k]   (token stride stride_q / stride_k elements)
+ *      v      [N_tok][H_v][d_v]   (token stride stride_v)
+ *      o      [N_tok][H_v][d_v]   (packed)
+ *      g,beta [N_tok][H_v]        fp32 (log-decay and write strength)
+ *      state  [N_seq][H_v][d_k][d_v] fp32
+ *    q/k/v/o/conv tensors are fp32 or bf16 (gdn_dims.dtype); gates and
+ *    states are always fp32 (the same notes: DeltaNet scalar parameters
+ *    stay F32 end to end).
+ *  - Pointers to bf16/fp32 tensors must be 16-byte aligned and token strides
+ *    multiples of 8 elements (bf16) or 4 (fp32), so rows load as 128-bit words.
+ *  - Errors: a gdn_status; gdn_last_error() gives a message for the calling
+ *    thread.  If the environment has GDN_DEBUG=1 the library also
+ *    synchronises after each call and scans outputs for NaN/Inf
+ *    (GDN_ERR_NONFINITE), in the spirit of the per-stage NaN/Inf probe the
+ *    oxydllm notes list under "GDN debug aids".
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* bad shape, null pointer, misalignment, bad flag */
+    GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim 96) */
+    GDN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 4,         /* a HIP runtime call failed */
+    GDN_ERR_NONFINITE = 5    /* GDN_DEBUG=1 only: NaN/Inf found in an output */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+enum {
+    /* q and k are L2-normalised per head before use: x / sqrt(|x|^2 + 1e-6). */
+    GDN_QK_L2NORM = 1u,
+    /* v-head h reads q/k head (h % H_k) -- the tiled V-head order that GGUF
+     * files use (oxydllm notes, "GGUF qwen35 architecture").  Default: head
+     * h / (H_v / H_k), the repeat-interleave order. */
+    GDN_HEADS_TILED = 2u
+};
+
+/* Problem description shared by the scan entry points. */
+typedef struct gdn_dims {
+    int32_t num_seqs;     /* N >= 1 */
+    int32_t total_tokens; /* N_tok = sum of sequence lengths (>= 0) */
+    int32_t seqlen;       /* > 0: every sequence has this length (dense, N_tok = N*seqlen);
+                             0: lengths come from cu_seqlens (varlen) */
+    int32_t num_qk_heads; /* H_k >= 1 */
+    int32_t num_v_heads;  /* H_v, a multiple of H_k */
+    int32_t head_dim_k;   /* d_k in {64, 128} */
+    int32_t head_dim_v;   /* d_v in {64, 128} (d_k != d_v allowed) */
+    int32_t chunk_size;   /* prefill chunk C in {16, 32, 64}; ignored by decode */
+    int32_t dtype;        /* gdn_dtype of q, k, v, o */
+    uint32_t flags;       /* GDN_QK_L2NORM | GDN_HEADS_TILED */
+    float scale;          /* multiplies q (after the L2 norm, if any) */
+    int32_t reserved;     /* must be 0 */
+    int64_t stride_q;     /* elements between consecutive tokens of q; 0 = H_k*d_k */
+    int64_t stride_k;     /* same for k; 0 = H_k*d_k */
+    int64_t stride_v;     /* same for v; 0 = H_v*d_v */
+} gdn_dims;
+
+/* Human-readable name of a status code (static storage). */
+const char *gdn_status_string(gdn_status s);
+
+/* Message describing the most recent error on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *gdn_version(void);
+
+/*
+ * Host-only check of a problem description, no GPU needed: the same shape
+ * rules the entry points apply before queuing anything (pointer and
+ * workspace checks happen in the entry points).  op: 0 = prefill, 1 = decode.
+ */
+gdn_status gdn_validate_dims(const gdn_dims *d, int32_t op);
+
+/*
+ * Causal depthwise conv1d (+ optional SiLU) over packed sequences.
+ *
+ * For sequence i and channel c, with x_i its tokens and w[c][0..W-1]:
+ *     y[t][c] = act( bias[c] + sum_{j=0}^{W-1} w[c][j] * xx[t - (W-1) + j][c] )
+ * where positions before the sequence start read the conv window
+ * conv_state[i][W-1 + pos][c] (slot W-2 is the newest), or zero when
+ * conv_state is NULL.  Tap W-1 multiplies the current token.  act is SiLU,
+ * a / (1 + e^{-a}), when activation == 1, identity when 0.  The sum is
+ * evaluated in fp32 as acc = bias (or 0), acc = fma(w_j, x_j, acc) for j = 0..W-1,
+ * with one fixed exponential, so results are bit-reproducible; bf16 outputs
+ * are rounded to nearest even.
+ *
+ * num_seqs, total_tokens, seqlen, cu_seqlens: as in gdn_dims (cu_seqlens is
+ * a device int32[N+1] array, required iff seqlen == 0).
+ * channels: C; width: W in [2, 8]; dtype: of x, y and conv_state.
+ * x: [N_tok] rows with token stride stride_x (>= C); y: [N_tok][C] rows
+ * with stride stride_y (>= C).  weight: fp32 [C][W]; bias: fp32 [C] or NULL.
+ * conv_state: [N][W-1][C] in dtype, in/out, or NULL: on return it holds the
+ * last W-1 raw inputs of (old window ++ sequence), ready for the next call.
+ * x and y must not overlap.  A sequence with zero tokens leaves its window
+ * unchanged.  With seqlen == 1 this is the decode-time conv step.
+ */
+gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen,
+                      const int32_t *cu_seqlens, int32_t channels, int32_t width,
+                      int32_t dtype, const void *x, int64_t stride_x,
+                      const float *weight, const float *bias, void *conv_state,
+                      int32_t activation, void *y, int64_t stride_y, void *stream);
+
+/*
+ * Device workspace (bytes) that gdn_prefill_chunked / gdn_prefill_prepare /
+ * gdn_prefill_scan need for this problem: the per-chunk inverses and the
+ * chunk table.  0 on invalid dims (gdn_last_error says why).
+ */
+size_t gdn_prefill_workspace_size(const gdn_dims *d);
+
+/*
+ * Chunked prefill of the gated delta rule (the chunked parallel scan of the
+ * oxydllm notes, "New Features"), for N sequences packed along tokens.
+ *
+ * q, k, v, g, beta: see the layout table above.  state_in: fp32
+ * [N][H_v][d_k][d_v] or NULL (zero state).  cu_seqlens: device int32 [N+1]
+ * (required iff d->seqlen == 0; each sequence is chunked from its own
+ * start).  o: [N_tok][H_v][d_v] in dtype.  state_out: fp32
+ * [N][H_v][d_k][d_v] or NULL (discarded); it may alias state_in exactly.
+ * workspace: >= gdn_prefill_workspace_size(d) bytes, 256-byte aligned.
+ *
+ * The result equals the token recurrence above up to rounding: per chunk,
+ * the unit-lower-triangular system (I + A) is inverted blockwise (a
+ * doubling product on 16x16 diagonal blocks, then pairwise merging of
+ * blocks -- the oxydllm notes' remedy for fp32 overflow of plain doubling
+ * on repeated tokens), the state-independent products are formed per chunk,
+ * and the state is carried across chunks sequentially in fp32.
+ * Equivalent to gdn_prefill_prepare followed by gdn_prefill_scan.
+ */
+gdn_status gdn_prefill_chunked(const gdn_dims *d, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta,
+                               const float *state_in, const int32_t *cu_seqlens,
+                               void *o, float *state_out, void *workspace,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * Phase 1 of the prefill: everything that does not depend on the carried
+ * state (the oxydllm notes, "Performance": the cross-chunk loop precomputes
+ * all state-independent work in batch).  For every chunk and v-head it
+ * writes Tinv(I + A) diag(beta) into the workspace; fully parallel over
+ * chunks.  Arguments as gdn_prefill_chunked.
+ */
+gdn_status gdn_prefill_prepare(const gdn_dims *d, const void *k, const float *g,
+                               const float *beta, const int32_t *cu_seqlens,
+                               void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Phase 2 of the prefill: the sequential carry over chunks, reading the
+ * workspace written by gdn_prefill_prepare for the same inputs, and writing
+ * o and state_out.  Arguments as gdn_prefill_chunked.
+ */
+gdn_status gdn_prefill_scan(const gdn_dims *d, const void *q, const void *k,
+                            const void *v, const float *g, const float *beta,
+                            const float *state_in, const int32_t *cu_seqlens,
+                            void *o, float *state_out, const void *workspace,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * One decode step (the O(1) recurrent step of the oxydllm notes): one new
+ * token for each of d->num_seqs sequences (d->seqlen must be 1 and
+ * d->total_tokens == d->num_seqs; chunk_size is ignored).
+ *
+ * q, k [B][H_k][d_k], v [B][H_v][d_v] (token strides from d), g, beta
+ * [B][H_v] fp32, o [B][H_v][d_v].  state: fp32 [num_slots][H_v][d_k][d_v],
+ * updated in place; sequence b uses slot state_slots[b] (device int32 [B])
+ * or slot b when state_slots is NULL (then num_slots >= B).  Two sequences
+ * must not share a slot.  A slot index outside [0, num_slots) is caught on
+ * the device: that sequence's output is set to NaN and no state is touched.
+ */
+gdn_status gdn_decode_step(const gdn_dims *d, const void *q, const void *k,
+                           const void *v, const float *g, const float *beta,
+                           float *state, int32_t num_slots,
+                           const int32_t *state_slots, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,276 @@
+// conv1d.hip -- causal depthwise conv1d (+SiLU) for the Gated DeltaNet
+// layer: the short convolution that produces q, k, v (Vallmo.jl README,
+// "What's here"; the oxydllm 0.0.0-alpha.12.2 notes, "New Features", keep
+// its window as per-sequence state).
+//
+// Bandwidth-bound: every input element is read once (plus a W-1 halo per
+// run of tokens) and every output written once.  A thread owns one 16-byte
+// vector of channels (8 bf16 or 4 fp32) and walks a run of TOK tokens with
+// the last W-1 inputs in registers, so rows are read with 128-bit loads and
+// consecutive threads touch consecutive 16-byte words.
+//
+// Bit-exact arithmetic: acc = bias (or 0); acc = fma(w_j, x_j, acc) for
+// j = 0..W-1; y = acc / (1 + exp_cw(-acc)); bf16 output rounded to nearest
+// even.  Contraction is switched off in this file so the compiler adds or
+// removes no fused multiply-adds.
+#pragma clang fp contract(off)
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <class E>
+struct Vec;  // 16 bytes of channels
+template <>
+struct Vec<BF16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, const float* v) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; i++) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = w;
+  }
+};
+template <>
+struct Vec<F32> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* out) {
+    f32x4 w = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[i] = w[i];
+  }
+  __device__ __forceinline__ static void store(float* p, const float* v) {
+    f32x4 w = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p) = w;
+  }
+};
+
+__device__ __forceinline__ float silu_exact(float a) { return a / (1.0f + exp_cw(-a)); }
+
+// Sequence containing token t: the last s with cu[s] <= t.
+__device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int t) {
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <class E, int W, int TOK>
+__global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
+  typedef typename E::store_t T;
+  constexpr int V = Vec<E>::N;
+  const int cg = blockIdx.y * blockDim.x + threadIdx.x;  // channel group
+  const int c0 = cg * V;
+  if (c0 >= a.channels) return;
+  const int t_begin = blockIdx.x * TOK;
+  if (t_begin >= a.total_tokens) return;
+  const int t_end = min(t_begin + TOK, a.total_tokens);
+
+  float w[V][W];
+  float bias[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+#pragma unroll
+    for (int j = 0; j < W; j++) w[i][j] = a.weight[(long)(c0 + i) * W + j];
+    bias[i] = a.bias ? a.bias[c0 + i] : 0.0f;
+  }
+  const T* x = reinterpret_cast<const T*>(a.x);
+  T* y = reinterpret_cast<T*>(a.y);
+  const T* win = reinterpret_cast<const T*>(a.conv_state);
+
+  int seq, seq_start, seq_end;
+  if (a.seqlen > 0) {
+    seq = t_begin / a.seqlen;
+    seq_start = seq * a.seqlen;
+    seq_end = seq_start + a.seqlen;
+  } else {
+    seq = find_seq(a.cu_seqlens, a.num_seqs, t_begin);
+    seq_start = a.cu_seqlens[seq];
+    seq_end = a.cu_seqlens[seq + 1];
+  }
+
+  // hist[j] = input at position t - (W-1) + j for the token t about to run
+  float hist[W][V];
+  auto fill_context = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < W - 1; j++) {
+      int pos = t - (W - 1) + j;  // absolute token index
+      if (pos >= seq_start) {
+        Vec<E>::load(x + (long)pos * a.stride_x + c0, hist[j]);
+      } else if (win) {
+        int slot = (W - 1) + (pos - seq_start);  // 0..W-2, W-2 newest
+        Vec<E>::load(win + ((long)seq * (W - 1) + slot) * a.channels + c0, hist[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; i++) hist[j][i] = 0.0f;
+      }
+    }
+  };
+  fill_context(t_begin);
+
+  for (int t = t_begin; t < t_end; t++) {
+    if (t == seq_end) {  // next sequence: fresh context
+      seq++;
+      if (a.seqlen > 0) {
+        seq_start = t;
+        seq_end = t + a.seqlen;
+      } else {
+        while (a.cu_seqlens[seq + 1] <= t) seq++;  // skip empty sequences
+        seq_start = a.cu_seqlens[seq];
+        seq_end = a.cu_seqlens[seq + 1];
+      }
+      fill_context(t);
+    }
+    Vec<E>::load(x + (long)t * a.stride_x + c0, hist[W - 1]);
+    float out[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      float acc = bias[i];
+#pragma unroll
+      for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], hist[j][i], acc);
+      out[i] = a.activation ? silu_exact(acc) : acc;
+    }
+    Vec<E>::store(y + (long)t * a.stride_y + c0, out);
+#pragma unroll
+    for (int j = 0; j < W - 1; j++)
+#pragma unroll
+      for (int i = 0; i < V; i++) hist[j][i] = hist[j + 1][i];
+  }
+}
+
+// New window = last W-1 raw inputs of (old window ++ sequence).  One thread
+// per (sequence, 16-byte channel group); it reads everything it needs before
+// writing, so the update is in place.  Runs after k_conv1d on the stream.
+template <class E, int W>
+__global__ void __launch_bounds__(256) k_conv_window(ConvArgs a) {
+  typedef typename E::store_t T;
+  constexpr int V = Vec<E>::N;
+  const int cg = blockIdx.y * blockDim.x + threadIdx.x;
+  const int c0 = cg * V;
+  const int seq = blockIdx.x;
+  if (c0 >= a.channels || seq >= a.num_seqs) return;
+  int s0, s1;
+  if (a.seqlen > 0) {
+    s0 = seq * a.seqlen;
+    s1 = s0 + a.seqlen;
+  } else {
+    s0 = a.cu_seqlens[seq];
+    s1 = a.cu_seqlens[seq + 1];
+  }
+  const int len = s1 - s0;
+  if (len == 0) return;
+  const T* x = reinterpret_cast<const T*>(a.x);
+  T* win = reinterpret_cast<T*>(a.conv_state);
+  T* mywin = win + (long)seq * (W - 1) * a.channels + c0;
+  float nw[W - 1][V];
+#pragma unroll
+  for (int i = 0; i < W - 1; i++) {
+    int pos = len - (W - 1) + i;  // position in the sequence
+    if (pos >= 0)
+      Vec<E>::load(x + (long)(s0 + pos) * a.stride_x + c0, nw[i]);
+    else
+      Vec<E>::load(mywin + (long)((W - 1) + pos) * a.channels, nw[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < W - 1; i++) Vec<E>::store(mywin + (long)i * a.channels, nw[i]);
+}
+
+// One token per sequence (decode): read window + token, write y and the
+// shifted window.  Same arithmetic as k_conv1d.
+template <class E, int W>
+__global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
+  typedef typename E::store_t T;
+  constexpr int V = Vec<E>::N;
+  const int cg = blockIdx.y * blockDim.x + threadIdx.x;
+  const int c0 = cg * V;
+  const int seq = blockIdx.x;
+  if (c0 >= a.channels || seq >= a.num_seqs) return;
+  const T* x = reinterpret_cast<const T*>(a.x);
+  T* y = reinterpret_cast<T*>(a.y);
+  T* win = reinterpret_cast<T*>(a.conv_state);
+  float hist[W][V];
+  if (win) {
+#pragma unroll
+    for (int j = 0; j < W - 1; j++)
+      Vec<E>::load(win + ((long)seq * (W - 1) + j) * a.channels + c0, hist[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < W - 1; j++)
+#pragma unroll
+      for (int i = 0; i < V; i++) hist[j][i] = 0.0f;
+  }
+  Vec<E>::load(x + (long)seq * a.stride_x + c0, hist[W - 1]);
+  float out[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) {
+    float acc = a.bias ? a.bias[c0 + i] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < W; j++) acc = __builtin_fmaf(a.weight[(long)(c0 + i) * W + j], hist[j][i], acc);
+    out[i] = a.activation ? silu_exact(acc) : acc;
+  }
+  Vec<E>::store(y + (long)seq * a.stride_y + c0, out);
+  if (win) {
+#pragma unroll
+    for (int j = 0; j < W - 1; j++)
+      Vec<E>::store(win + ((long)seq * (W - 1) + j) * a.channels + c0, hist[j + 1]);
+  }
+}
+
+constexpr int kConvTok = 16;
+
+template <class E, int W>
+hipError_t launch_w(const ConvArgs& a, hipStream_t s) {
+  constexpr int V = Vec<E>::N;
+  const int groups = a.channels / V;
+  dim3 block(256);
+  if (a.seqlen == 1) {
+    dim3 grid(a.num_seqs, (groups + 255) / 256);
+    if (a.num_seqs > 0) hipLaunchKernelGGL((k_conv_step<E, W>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.total_tokens > 0) {
+    dim3 grid((a.total_tokens + kConvTok - 1) / kConvTok, (groups + 255) / 256);
+    hipLaunchKernelGGL((k_conv1d<E, W, kConvTok>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.conv_state && a.num_seqs > 0) {
+    dim3 grid(a.num_seqs, (groups + 255) / 256);
+    hipLaunchKernelGGL((k_conv_window<E, W>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_e(const ConvArgs& a, hipStream_t s) {
+  switch (a.width) {
+    case 2: return launch_w<E, 2>(a, s);
+    case 3: return launch_w<E, 3>(a, s);
+    case 4: return launch_w<E, 4>(a, s);
+    case 5: return launch_w<E, 5>(a, s);
+    case 6: return launch_w<E, 6>(a, s);
+    case 7: return launch_w<E, 7>(a, s);
+    case 8: return launch_w<E, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s) {
+  return a.dtype == 1 ? launch_e<BF16>(a, s) : launch_e<F32>(a, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,381 @@
+// gdn_api.cpp -- the C ABI of libgdn (declared in include/gdn.h): argument
+// validation, workspace carving and kernel dispatch.  Every check runs on
+// the host before any HIP call, so an invalid call queues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool debug_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("GDN_DEBUG");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+constexpr int64_t kMaxTokens = 1LL << 30;
+
+gdn_status check_dims(const gdn_dims* d, int op) {
+  if (!d) return fail(GDN_ERR_INVALID_ARG, "dims is NULL");
+  if (d->reserved != 0) return fail(GDN_ERR_INVALID_ARG, "dims.reserved must be 0");
+  if (d->num_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", d->num_seqs);
+  if (d->total_tokens < 0 || d->total_tokens > kMaxTokens)
+    return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range (got %d)", d->total_tokens);
+  if (d->seqlen < 0) return fail(GDN_ERR_INVALID_ARG, "seqlen must be >= 0 (got %d)", d->seqlen);
+  if (d->seqlen > 0 && (int64_t)d->num_seqs * d->seqlen != d->total_tokens)
+    return fail(GDN_ERR_INVALID_ARG, "dense layout needs total_tokens == num_seqs * seqlen (%d != %d * %d)",
+                d->total_tokens, d->num_seqs, d->seqlen);
+  if (d->num_qk_heads < 1) return fail(GDN_ERR_INVALID_ARG, "num_qk_heads must be >= 1");
+  if (d->num_v_heads < d->num_qk_heads || d->num_v_heads % d->num_qk_heads != 0)
+    return fail(GDN_ERR_INVALID_ARG, "num_v_heads (%d) must be a positive multiple of num_qk_heads (%d)",
+                d->num_v_heads, d->num_qk_heads);
+  if (d->num_v_heads > 4096) return fail(GDN_ERR_UNSUPPORTED, "num_v_heads > 4096");
+  if (d->head_dim_k <= 0 || d->head_dim_v <= 0)
+    return fail(GDN_ERR_INVALID_ARG, "head dims must be positive");
+  if ((d->head_dim_k != 64 && d->head_dim_k != 128) || (d->head_dim_v != 64 && d->head_dim_v != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "head dims must be 64 or 128 (got d_k=%d, d_v=%d)", d->head_dim_k,
+                d->head_dim_v);
+  if (d->dtype != GDN_F32 && d->dtype != GDN_BF16) return fail(GDN_ERR_INVALID_ARG, "dtype must be GDN_F32 or GDN_BF16");
+  if (d->flags & ~(uint32_t)(GDN_QK_L2NORM | GDN_HEADS_TILED))
+    return fail(GDN_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  if (!std::isfinite(d->scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+  const int64_t vec = d->dtype == GDN_BF16 ? 8 : 4;
+  const int64_t qk_row = (int64_t)d->num_qk_heads * d->head_dim_k;
+  const int64_t v_row = (int64_t)d->num_v_heads * d->head_dim_v;
+  const int64_t sq = d->stride_q ? d->stride_q : qk_row;
+  const int64_t sk = d->stride_k ? d->stride_k : qk_row;
+  const int64_t sv = d->stride_v ? d->stride_v : v_row;
+  if (sq < qk_row || sk < qk_row || sv < v_row)
+    return fail(GDN_ERR_INVALID_ARG, "token strides must cover a whole row (q %lld, k %lld >= %lld; v %lld >= %lld)",
+                (long long)sq, (long long)sk, (long long)qk_row, (long long)sv, (long long)v_row);
+  if (sq % vec || sk % vec || sv % vec)
+    return fail(GDN_ERR_INVALID_ARG, "token strides must be multiples of %lld elements", (long long)vec);
+  if (op == 0) {
+    if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
+      return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64 (got %d)", d->chunk_size);
+  } else if (op == 1) {
+    if (d->seqlen != 1 || d->total_tokens != d->num_seqs)
+      return fail(GDN_ERR_INVALID_ARG, "decode needs seqlen == 1 and total_tokens == num_seqs");
+  } else {
+    return fail(GDN_ERR_INVALID_ARG, "op must be 0 (prefill) or 1 (decode)");
+  }
+  return ok();
+}
+
+int64_t max_chunks(const gdn_dims* d) {
+  const int64_t C = d->chunk_size;
+  if (d->seqlen > 0) return (int64_t)d->num_seqs * ((d->seqlen + C - 1) / C);
+  return (int64_t)d->total_tokens / C + d->num_seqs;
+}
+
+struct WsLayout {
+  size_t table_off, table_bytes, tinv_off, tinv_bytes, total;
+};
+
+WsLayout ws_layout(const gdn_dims* d) {
+  WsLayout w;
+  w.table_off = 0;
+  w.table_bytes = d->seqlen > 0 ? 0 : (((size_t)(d->num_seqs + 1) * 4 + 255) / 256) * 256;
+  w.tinv_off = w.table_bytes;
+  w.tinv_bytes = (size_t)max_chunks(d) * d->num_v_heads * d->chunk_size * d->chunk_size * elem_size(d->dtype);
+  w.total = w.tinv_off + w.tinv_bytes;
+  return w;
+}
+
+gdn::ScanArgs make_args(const gdn_dims* d) {
+  gdn::ScanArgs a;
+  memset(&a, 0, sizeof(a));
+  a.num_seqs = d->num_seqs;
+  a.total_tokens = d->total_tokens;
+  a.seqlen = d->seqlen;
+  a.hk = d->num_qk_heads;
+  a.hv = d->num_v_heads;
+  a.dk = d->head_dim_k;
+  a.dv = d->head_dim_v;
+  a.chunk = d->chunk_size;
+  a.dtype = d->dtype;
+  a.l2norm = (d->flags & GDN_QK_L2NORM) ? 1 : 0;
+  a.tiled = (d->flags & GDN_HEADS_TILED) ? 1 : 0;
+  a.scale = d->scale;
+  a.stride_q = d->stride_q ? d->stride_q : (long)d->num_qk_heads * d->head_dim_k;
+  a.stride_k = d->stride_k ? d->stride_k : (long)d->num_qk_heads * d->head_dim_k;
+  a.stride_v = d->stride_v ? d->stride_v : (long)d->num_v_heads * d->head_dim_v;
+  return a;
+}
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- GDN_DEBUG probe: the count lives in a file-scope device variable.
+__device__ int g_nonfinite_count;
+
+gdn_status debug_check(hipStream_t s, const char* what, const void* p, long n, int dtype) {
+  if (!debug_enabled() || !p || n <= 0) return GDN_OK;
+  int* dcount = nullptr;
+  hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&dcount), HIP_SYMBOL(g_nonfinite_count));
+  if (e != hipSuccess) return hip_fail(e, "GDN_DEBUG symbol");
+  int zero = 0, count = 0;
+  if ((e = hipMemcpyAsync(dcount, &zero, sizeof(int), hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = gdn::launch_nonfinite_probe(p, n, dtype, dcount, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(&count, dcount, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+      (e = hipStreamSynchronize(s)) != hipSuccess)
+    return hip_fail(e, "GDN_DEBUG probe");
+  if (count) return fail(GDN_ERR_NONFINITE, "GDN_DEBUG: %d non-finite values in %s", count, what);
+  return GDN_OK;
+}
+
+gdn_status check_scan_ptrs(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu, bool need_qv) {
+  if (d->total_tokens > 0) {
+    if (!k || !g || !beta || (need_qv && (!q || !v)))
+      return fail(GDN_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
+    if (!aligned(k, 16) || (need_qv && (!aligned(q, 16) || !aligned(v, 16))))
+      return fail(GDN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_INVALID_ARG, "g and beta must be 4-byte aligned");
+  }
+  if (d->seqlen == 0 && (!cu || !aligned(cu, 4)))
+    return fail(GDN_ERR_INVALID_ARG, "varlen (seqlen == 0) needs a 4-byte aligned cu_seqlens");
+  return GDN_OK;
+}
+
+gdn_status check_workspace(const gdn_dims* d, const void* ws, size_t ws_bytes) {
+  const WsLayout L = ws_layout(d);
+  if (L.total > 0 && !ws) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if (ws && !aligned(ws, 256)) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total) return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  return GDN_OK;
+}
+
+void carve(gdn::ScanArgs& a, const gdn_dims* d, const void* ws) {
+  const WsLayout L = ws_layout(d);
+  char* base = reinterpret_cast<char*>(const_cast<void*>(ws));
+  a.chunk_offsets = L.table_bytes ? reinterpret_cast<int32_t*>(base + L.table_off) : nullptr;
+  a.tinv = base ? base + L.tinv_off : nullptr;
+  a.max_chunks = (int)max_chunks(d);
+}
+
+gdn_status run_prepare(gdn::ScanArgs& a, hipStream_t s) {
+  hipError_t e;
+  if (a.seqlen == 0 && (e = gdn::launch_chunk_table(a, s)) != hipSuccess) return hip_fail(e, "chunk table launch");
+  if (a.total_tokens > 0 && (e = gdn::launch_prepare(a, s)) != hipSuccess) return hip_fail(e, "prepare launch");
+  return GDN_OK;
+}
+
+gdn_status run_scan(gdn::ScanArgs& a, const gdn_dims* d, hipStream_t s) {
+  hipError_t e = gdn::launch_scan(a, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  gdn_status st = debug_check(s, "o", a.o, (long)d->total_tokens * d->num_v_heads * d->head_dim_v, d->dtype);
+  if (st != GDN_OK) return st;
+  return debug_check(s, "state_out", a.state_out, (long)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v,
+                     GDN_F32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    case GDN_ERR_NONFINITE: return "GDN_ERR_NONFINITE";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+gdn_status gdn_validate_dims(const gdn_dims* d, int32_t op) { return check_dims(d, op); }
+
+gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen, const int32_t* cu_seqlens,
+                      int32_t channels, int32_t width, int32_t dtype, const void* x, int64_t stride_x,
+                      const float* weight, const float* bias, void* conv_state, int32_t activation, void* y,
+                      int64_t stride_y, void* stream) {
+  if (num_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "num_seqs must be >= 1");
+  if (total_tokens < 0 || total_tokens > kMaxTokens) return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range");
+  if (seqlen < 0) return fail(GDN_ERR_INVALID_ARG, "seqlen must be >= 0");
+  if (seqlen > 0 && (int64_t)num_seqs * seqlen != total_tokens)
+    return fail(GDN_ERR_INVALID_ARG, "dense layout needs total_tokens == num_seqs * seqlen");
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_INVALID_ARG, "dtype must be GDN_F32 or GDN_BF16");
+  const int vec = dtype == GDN_BF16 ? 8 : 4;
+  if (channels < 1 || channels % vec) return fail(GDN_ERR_INVALID_ARG, "channels must be a positive multiple of %d", vec);
+  if (width < 2 || width > 8) return fail(GDN_ERR_UNSUPPORTED, "width must be in [2, 8] (got %d)", width);
+  if (activation != 0 && activation != 1) return fail(GDN_ERR_INVALID_ARG, "activation must be 0 or 1");
+  if (stride_x < channels || stride_y < channels || stride_x % vec || stride_y % vec)
+    return fail(GDN_ERR_INVALID_ARG, "strides must be >= channels and multiples of %d", vec);
+  if (total_tokens > 0) {
+    if (!x || !y) return fail(GDN_ERR_INVALID_ARG, "x and y must be non-NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(GDN_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  }
+  if (!weight || !aligned(weight, 4)) return fail(GDN_ERR_INVALID_ARG, "weight must be non-NULL and 4-byte aligned");
+  if (bias && !aligned(bias, 4)) return fail(GDN_ERR_INVALID_ARG, "bias must be 4-byte aligned");
+  if (conv_state && !aligned(conv_state, 16)) return fail(GDN_ERR_INVALID_ARG, "conv_state must be 16-byte aligned");
+  if (seqlen == 0 && (!cu_seqlens || !aligned(cu_seqlens, 4)))
+    return fail(GDN_ERR_INVALID_ARG, "varlen (seqlen == 0) needs a 4-byte aligned cu_seqlens");
+  gdn::ConvArgs a;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.seqlen = seqlen;
+  a.cu_seqlens = cu_seqlens;
+  a.channels = channels;
+  a.width = width;
+  a.dtype = dtype;
+  a.activation = activation;
+  a.x = x;
+  a.stride_x = stride_x;
+  a.weight = weight;
+  a.bias = bias;
+  a.conv_state = conv_state;
+  a.y = y;
+  a.stride_y = stride_y;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_conv1d(a, s);
+  if (e != hipSuccess) return hip_fail(e, "conv1d launch");
+  if (debug_enabled() && total_tokens > 0) {
+    // y rows may be strided: probe the whole span (padding included)
+    gdn_status st = debug_check(s, "conv y", y, (long)(total_tokens - 1) * stride_y + channels, dtype);
+    if (st != GDN_OK) return st;
+  }
+  return ok();
+}
+
+size_t gdn_prefill_workspace_size(const gdn_dims* d) {
+  if (check_dims(d, 0) != GDN_OK) return 0;
+  return ws_layout(d).total;
+}
+
+gdn_status gdn_prefill_prepare(const gdn_dims* d, const void* k, const float* g, const float* beta,
+                               const int32_t* cu_seqlens, void* workspace, size_t ws_bytes, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, nullptr, k, nullptr, g, beta, cu_seqlens, false)) != GDN_OK) return st;
+  if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
+  gdn::ScanArgs a = make_args(d);
+  a.k = k;
+  a.g = g;
+  a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  carve(a, d, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = run_prepare(a, s)) != GDN_OK) return st;
+  return ok();
+}
+
+gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
+                            float* state_out, const void* workspace, size_t ws_bytes, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true)) != GDN_OK) return st;
+  if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
+  if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
+  if (state_in && state_out && state_in != state_out) {
+    const size_t sbytes = (size_t)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v * 4;
+    const char* a0 = reinterpret_cast<const char*>(state_in);
+    const char* b0 = reinterpret_cast<const char*>(state_out);
+    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
+      return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
+  }
+  gdn::ScanArgs a = make_args(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.state_out = state_out;
+  carve(a, d, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = run_scan(a, d, s)) != GDN_OK) return st;
+  return ok();
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
+                               float* state_out, void* workspace, size_t ws_bytes, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true)) != GDN_OK) return st;
+  if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
+  // validate the scan half fully before queuing the prepare half
+  if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
+  if ((st = gdn_prefill_prepare(d, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
+  return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, int32_t num_slots, const int32_t* state_slots, void* o,
+                           void* stream) {
+  gdn_status st = check_dims(d, 1);
+  if (st != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, v, g, beta, nullptr, true)) != GDN_OK) return st;
+  if (!o || !aligned(o, 16)) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
+  if (!state || !aligned(state, 16)) return fail(GDN_ERR_INVALID_ARG, "state must be non-NULL and 16-byte aligned");
+  if (num_slots < 1) return fail(GDN_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (!state_slots && num_slots < d->num_seqs)
+    return fail(GDN_ERR_INVALID_ARG, "without state_slots, num_slots (%d) must be >= num_seqs (%d)", num_slots,
+                d->num_seqs);
+  if (state_slots && !aligned(state_slots, 4)) return fail(GDN_ERR_INVALID_ARG, "state_slots must be 4-byte aligned");
+  gdn::ScanArgs a = make_args(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.state = state;
+  a.state_slots = state_slots;
+  a.num_slots = num_slots;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_decode(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if ((st = debug_check(s, "o", o, (long)d->num_seqs * d->num_v_heads * d->head_dim_v, d->dtype)) != GDN_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// gdn_device.h -- device helpers for the gfx950 kernels of libgdn.
+//
+// bf16 handling, 128-bit vector types, the matrix-core (MFMA) tile
+// primitive, wave-level reductions and the fp32 exponential the
+// convolution uses.
+//
+// MFMA operand layout on gfx950 (64-lane wave), for D(16x16) += A(16xK) B(Kx16):
+//   A: lane l holds row (l % 16), k = kb + KPL*(l / 16) + e, e < KPL
+//   B: lane l holds col (l % 16), k = kb + KPL*(l / 16) + e
+//   D: lane l holds col (l % 16), rows 4*(l / 16) + e, e < 4
+// with KPL = 8 (v_mfma_f32_16x16x32_bf16, K step 32) or KPL = 1
+// (v_mfma_f32_16x16x4_f32, K step 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element traits: storage type of q/k/v/o and of the MFMA operands.
+struct BF16 {
+  typedef uint16_t store_t;
+  static constexpr int KPL = 8;    // operand elements per lane
+  static constexpr int KSTEP = 32; // K covered by one MFMA
+  typedef bf16x8 frag_t;
+  __device__ __forceinline__ static float to_f32(store_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static store_t from_f32(float f) { return f32_to_bf16(f); }
+};
+
+struct F32 {
+  typedef float store_t;
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 4;
+  typedef float frag_t;
+  __device__ __forceinline__ static float to_f32(store_t v) { return v; }
+  __device__ __forceinline__ static store_t from_f32(float f) { return f; }
+};
+
+// Load one MFMA operand fragment: KPL consecutive elements starting at p
+// (p must be 16-byte aligned for bf16).
+__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p, BF16) {
+  u32x4 w = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ float load_frag(const float* p, F32) { return *p; }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// D += A[row0.., k0..k0+K) * B[k0..k0+K), col0..) where A is row-major with
+// leading dimension lda and B is given TRANSPOSED (BT row-major [col][k],
+// leading dimension ldb) -- both operands then read KPL contiguous elements.
+template <class E, int K>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const typename E::store_t* A, int lda,
+                                          const typename E::store_t* BT, int ldb, int lane) {
+  const int r = lane & 15, kq = (lane >> 4) * E::KPL;
+  const typename E::store_t* pa = A + r * lda + kq;
+  const typename E::store_t* pb = BT + r * ldb + kq;
+#pragma unroll
+  for (int kb = 0; kb < K; kb += E::KSTEP) {
+    acc = mfma16(load_frag(pa + kb, E()), load_frag(pb + kb, E()), acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Make this wave's earlier LDS writes visible to its later LDS reads
+// (other lanes of the same wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------- fixed fp32 exponential
+//
+// e^x by Cody & Waite's method ("Software Manual for the Elementary
+// Functions", 1980): x = n ln2 + r, n = rint(x / ln2), r = (x - n C1) - n C2
+// with C1 = ln2 cut to 16 significant bits (n C1 exact for |n| < 256) and
+// C2 = fp32(ln2 - C1); e^r by its Taylor series through r^7 in Horner form
+// with fused multiply-adds; then scaled by 2^n.  Inputs above 88.5 give
+// +inf, below -86 give 0, so every finite result is a normal number.  The
+// operation order is fixed so that the convolution's output is a function of
+// its inputs alone, reproducible bit for bit by any IEEE fp32 machine that
+// follows the same steps.
+__device__ __forceinline__ float exp_cw(float x) {
+  if (x != x) return x;
+  if (x > 88.5f) return __builtin_inff();
+  if (x < -86.0f) return 0.0f;
+  const float c1 = 0.693145751953125f;          // 45426 / 65536
+  const float c2 = (float)(0.69314718055994530942 - 0.693145751953125);
+  const float inv_ln2 = (float)(1.0 / 0.69314718055994530942);
+  float n = __builtin_rintf(x * inv_ln2);
+  float r = __builtin_fmaf(-n, c1, x);
+  r = __builtin_fmaf(-n, c2, r);
+  float p = (float)(1.0 / 5040.0);
+  p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+}  // namespace gdn

@@ -1,0 +1,59 @@
+// gdn_internal.h -- argument blocks and kernel launchers shared between the
+// C-ABI layer (gdn_api.cpp) and the kernels (*.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ConvArgs {
+  int num_seqs, total_tokens, seqlen;
+  const int32_t* cu_seqlens;
+  int channels, width, dtype, activation;
+  const void* x;
+  long stride_x;
+  const float* weight;
+  const float* bias;
+  void* conv_state;
+  void* y;
+  long stride_y;
+};
+
+// Everything the scan kernels need; pointers are device pointers.
+struct ScanArgs {
+  int num_seqs, total_tokens, seqlen;  // seqlen > 0: dense
+  int hk, hv, dk, dv, chunk;           // heads, head dims, chunk size
+  int dtype;                           // 0 f32, 1 bf16
+  int l2norm, tiled;
+  float scale;
+  long stride_q, stride_k, stride_v;   // elements between tokens
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* state_in;
+  const int32_t* cu_seqlens;  // varlen only
+  void* o;
+  float* state_out;
+  // workspace carve-up
+  int32_t* chunk_offsets;     // [num_seqs + 1], varlen only
+  void* tinv;                 // [max_chunks][hv][chunk][chunk] in the operand type
+  int max_chunks;
+  // decode only
+  float* state;
+  const int32_t* state_slots;
+  int num_slots;
+};
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
+hipError_t launch_chunk_table(const ScanArgs& a, hipStream_t s);
+hipError_t launch_prepare(const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_decode(const ScanArgs& a, hipStream_t s);
+// GDN_DEBUG: count non-finite values (fp32 or bf16) into *count (device int).
+hipError_t launch_nonfinite_probe(const void* p, long n, int dtype, int* count, hipStream_t s);
+
+}  // namespace gdn

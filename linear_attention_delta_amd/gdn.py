@@ -1,0 +1,232 @@
+"""Thin ctypes binding of libgdn (include/gdn.h).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  Tensors are torch CUDA (HIP) tensors used for device memory;
+the binding passes their data pointers and the current stream.  If
+libgdn.so is missing this module raises at import -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_F32 = 0
+GDN_BF16 = 1
+GDN_QK_L2NORM = 1
+GDN_HEADS_TILED = 2
+OP_PREFILL = 0
+OP_DECODE = 1
+
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_WORKSPACE",
+                4: "GDN_ERR_HIP", 5: "GDN_ERR_NONFINITE"}
+
+EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
+            "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
+            "gdn_decode_step"]
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+        ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64), ("stride_v", ctypes.c_int64),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m linear_attention_delta_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(GdnDims)
+    sig = {
+        "gdn_status_string": ([i32], ctypes.c_char_p),
+        "gdn_last_error": ([], ctypes.c_char_p),
+        "gdn_version": ([], ctypes.c_char_p),
+        "gdn_validate_dims": ([D, i32], i32),
+        "gdn_conv1d": ([i32, i32, i32, P, i32, i32, i32, P, i64, P, P, P, i32, P, i64, P], i32),
+        "gdn_prefill_workspace_size": ([D], sz),
+        "gdn_prefill_chunked": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gdn_prefill_prepare": ([D, P, P, P, P, P, sz, P], i32),
+        "gdn_prefill_scan": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.gdn_last_error().decode()
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, last_error())
+
+
+def make_dims(*, num_seqs, total_tokens, seqlen, num_qk_heads, num_v_heads, head_dim_k, head_dim_v,
+              chunk_size=64, dtype=GDN_BF16, l2norm=True, heads_tiled=False, scale=1.0,
+              stride_q=0, stride_k=0, stride_v=0) -> GdnDims:
+    flags = (GDN_QK_L2NORM if l2norm else 0) | (GDN_HEADS_TILED if heads_tiled else 0)
+    return GdnDims(num_seqs, total_tokens, seqlen, num_qk_heads, num_v_heads, head_dim_k, head_dim_v,
+                   chunk_size, dtype, flags, scale, 0, stride_q, stride_k, stride_v)
+
+
+def validate_dims(d: GdnDims, op: int) -> int:
+    return int(lib.gdn_validate_dims(ctypes.byref(d), op))
+
+
+# ---- torch helpers (memory and streams only) -----------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _row_stride(t) -> int:
+    """Elements between consecutive tokens of a [N, H, d] (or [N, H*d]) view
+    whose inner dims are packed."""
+    return t.stride(0)
+
+
+def conv1d(x, weight, *, cu_seqlens=None, seqlen=None, num_seqs=None, bias=None, conv_state=None,
+           activation=True, out=None, stream=None):
+    """Causal depthwise conv (+SiLU).  x [N_tok, C] (rows may be strided),
+    weight fp32 [C, W].  Dense if seqlen is given (num_seqs = N_tok // seqlen),
+    varlen if cu_seqlens (device int32 [N+1]) is given.  Returns y [N_tok, C]."""
+    import torch
+    n_tok, C = x.shape
+    if out is None:
+        out = torch.empty((n_tok, C), dtype=x.dtype, device=x.device)
+    if cu_seqlens is not None:
+        n_seq = cu_seqlens.numel() - 1
+        sl = 0
+    else:
+        sl = int(seqlen if seqlen is not None else n_tok)
+        n_seq = int(num_seqs if num_seqs is not None else (n_tok // sl if sl else 1))
+    _check(lib.gdn_conv1d(n_seq, n_tok, sl, _ptr(cu_seqlens), C, weight.shape[1], _dtype_code(x),
+                          _ptr(x), x.stride(0), _ptr(weight), _ptr(bias), _ptr(conv_state),
+                          1 if activation else 0, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def _dims_for(q, k, v, *, num_seqs, seqlen, chunk_size, l2norm, heads_tiled, scale):
+    n_tok, hk, dk = q.shape
+    _, hv, dv = v.shape
+    return make_dims(num_seqs=num_seqs, total_tokens=n_tok, seqlen=seqlen, num_qk_heads=hk, num_v_heads=hv,
+                     head_dim_k=dk, head_dim_v=dv, chunk_size=chunk_size, dtype=_dtype_code(q),
+                     l2norm=l2norm, heads_tiled=heads_tiled, scale=scale,
+                     stride_q=_row_stride(q), stride_k=_row_stride(k), stride_v=_row_stride(v))
+
+
+def workspace_size(d: GdnDims) -> int:
+    n = int(lib.gdn_prefill_workspace_size(ctypes.byref(d)))
+    if n == 0 and validate_dims(d, OP_PREFILL) != GDN_OK:
+        raise GdnError(validate_dims(d, OP_PREFILL), last_error())
+    return n
+
+
+def alloc_workspace(d: GdnDims, device="cuda"):
+    import torch
+    n = workspace_size(d)
+    return torch.empty(max(n, 256) // 4 + 64, dtype=torch.int32, device=device)  # 256-aligned by torch
+
+
+class Prefill:
+    """Bound prefill problem: dims + workspace, reusable across calls."""
+
+    def __init__(self, q, k, v, *, cu_seqlens=None, seqlen=None, num_seqs=None, chunk_size=64,
+                 l2norm=True, heads_tiled=False, scale=1.0, workspace=None):
+        n_tok = q.shape[0]
+        if cu_seqlens is not None:
+            num_seqs = cu_seqlens.numel() - 1
+            seqlen = 0
+        else:
+            seqlen = int(seqlen if seqlen is not None else n_tok)
+            num_seqs = int(num_seqs if num_seqs is not None else (n_tok // seqlen if seqlen else 1))
+        self.dims = _dims_for(q, k, v, num_seqs=num_seqs, seqlen=seqlen, chunk_size=chunk_size,
+                              l2norm=l2norm, heads_tiled=heads_tiled, scale=scale)
+        self.cu_seqlens = cu_seqlens
+        self.ws = workspace if workspace is not None else alloc_workspace(self.dims, q.device)
+        self.ws_bytes = self.ws.numel() * self.ws.element_size()
+
+    def prepare(self, k, g, beta, stream=None):
+        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(k), _ptr(g), _ptr(beta),
+                                       _ptr(self.cu_seqlens), _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def scan(self, q, k, v, g, beta, o, state_in=None, state_out=None, stream=None):
+        _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state_in), _ptr(self.cu_seqlens), _ptr(o), _ptr(state_out),
+                                    _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def __call__(self, q, k, v, g, beta, o, state_in=None, state_out=None, stream=None):
+        _check(lib.gdn_prefill_chunked(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(state_in), _ptr(self.cu_seqlens), _ptr(o), _ptr(state_out),
+                                       _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+
+def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, num_seqs=None, chunk_size=64,
+            l2norm=True, heads_tiled=False, scale=1.0, want_state=True, out=None, state_out=None, stream=None):
+    """Chunked prefill.  q, k [N_tok, H_k, d_k]; v [N_tok, H_v, d_v] (token
+    rows may be strided views); g, beta fp32 [N_tok, H_v].  Returns (o, state)."""
+    import torch
+    p = Prefill(q, k, v, cu_seqlens=cu_seqlens, seqlen=seqlen, num_seqs=num_seqs, chunk_size=chunk_size,
+                l2norm=l2norm, heads_tiled=heads_tiled, scale=scale)
+    n_tok, hv, dv = v.shape
+    if out is None:
+        out = torch.empty((n_tok, hv, dv), dtype=q.dtype, device=q.device)
+    if state_out is None and want_state:
+        state_out = torch.empty((p.dims.num_seqs, hv, q.shape[2], dv), dtype=torch.float32, device=q.device)
+    p(q, k, v, g, beta, out, state_in, state_out, stream)
+    return out, state_out
+
+
+def decode_step(q, k, v, g, beta, state, *, state_slots=None, l2norm=True, heads_tiled=False, scale=1.0,
+                out=None, stream=None):
+    """One token per sequence.  q, k [B, H_k, d_k]; v [B, H_v, d_v]; g, beta
+    fp32 [B, H_v]; state fp32 [slots, H_v, d_k, d_v] updated in place."""
+    import torch
+    B, hk, dk = q.shape
+    _, hv, dv = v.shape
+    d = _dims_for(q, k, v, num_seqs=B, seqlen=1, chunk_size=64, l2norm=l2norm, heads_tiled=heads_tiled,
+                  scale=scale)
+    if out is None:
+        out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
+    _check(lib.gdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                               state.shape[0], _ptr(state_slots), _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,123 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/gdn.h
+declares, and its host-side validation rejects bad problems.  No kernel is
+launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def g():
+    from linear_attention_delta_amd import gdn
+    return gdn
+
+
+def test_library_exports_every_declared_symbol(g):
+    names = _header_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(g.lib, n)
+    assert sorted(g.EXPORTED) == names
+
+
+def test_status_strings(g):
+    for code, name in g.STATUS_NAMES.items():
+        assert g.lib.gdn_status_string(code).decode() == name
+    assert g.lib.gdn_version().decode().count(".") == 2
+
+
+def _dims(g, **kw):
+    base = dict(num_seqs=1, total_tokens=4096, seqlen=4096, num_qk_heads=16, num_v_heads=32, head_dim_k=128,
+                head_dim_v=128, chunk_size=64, dtype=g.GDN_BF16)
+    base.update(kw)
+    return g.make_dims(**base)
+
+
+def test_valid_problems_pass(g):
+    for kw in [{}, dict(dtype=g.GDN_F32), dict(chunk_size=16), dict(chunk_size=32), dict(head_dim_k=64),
+               dict(head_dim_v=64), dict(seqlen=0, total_tokens=70000, num_seqs=16),
+               dict(num_seqs=4, total_tokens=4 * 100, seqlen=100), dict(total_tokens=0, seqlen=0),
+               dict(stride_q=8192, stride_k=8192, stride_v=8192), dict(heads_tiled=True, l2norm=False)]:
+        assert g.validate_dims(_dims(g, **kw), g.OP_PREFILL) == g.GDN_OK, (kw, g.last_error())
+    assert g.validate_dims(_dims(g, num_seqs=64, total_tokens=64, seqlen=1), g.OP_DECODE) == g.GDN_OK
+
+
+BAD = [
+    (dict(num_seqs=0), 1), (dict(total_tokens=-1), 1), (dict(seqlen=-2), 1),
+    (dict(total_tokens=4095), 1),                       # dense: N * T mismatch
+    (dict(num_qk_heads=0), 1), (dict(num_v_heads=24), 1), (dict(num_v_heads=8), 1),
+    (dict(head_dim_k=96), 2), (dict(head_dim_v=256), 2), (dict(head_dim_k=0), 1),
+    (dict(chunk_size=48), 2), (dict(chunk_size=128), 2), (dict(dtype=7), 1),
+    (dict(stride_q=100), 1), (dict(stride_v=4100), 1),  # too short / misaligned
+    (dict(stride_k=2052), 1),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_invalid_problems_rejected(g, kw, code):
+    d = _dims(g, **kw)
+    assert g.validate_dims(d, g.OP_PREFILL) == code
+    assert g.last_error()
+
+
+def test_flags_scale_reserved(g):
+    d = _dims(g)
+    d.flags = 4
+    assert g.validate_dims(d, 0) == 1
+    d = _dims(g)
+    d.scale = float("nan")
+    assert g.validate_dims(d, 0) == 1
+    d = _dims(g)
+    d.reserved = 1
+    assert g.validate_dims(d, 0) == 1
+    assert g.lib.gdn_validate_dims(None, 0) == 1
+    assert g.validate_dims(_dims(g), 2) == 1
+    assert g.validate_dims(_dims(g), g.OP_DECODE) == 1   # decode needs seqlen 1
+
+
+def test_workspace_size(g):
+    d = _dims(g)                       # dense: 64 chunks x 32 heads x 64 x 64 bf16
+    assert g.workspace_size(d) == 64 * 32 * 64 * 64 * 2
+    d = _dims(g, dtype=g.GDN_F32, chunk_size=32, seqlen=100, num_seqs=3, total_tokens=300)
+    assert g.workspace_size(d) == 3 * 4 * 32 * 32 * 32 * 4
+    d = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5)   # varlen: table + upper bound of chunks
+    assert g.workspace_size(d) == 256 + (1000 // 64 + 5) * 32 * 64 * 64 * 2
+    assert g.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(g, chunk_size=8))) == 0
+
+
+def test_entry_points_reject_before_any_gpu_call(g):
+    """Invalid calls fail in host validation (these would need a GPU otherwise)."""
+    L = g.lib
+    assert L.gdn_conv1d(0, 10, 10, None, 64, 4, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 1
+    assert L.gdn_conv1d(1, 10, 10, None, 60, 4, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 1   # C % 8
+    assert L.gdn_conv1d(1, 10, 10, None, 64, 9, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 2   # width
+    assert L.gdn_conv1d(1, 10, 10, None, 64, 4, 1, 18, 64, 16, None, None, 1, 16, 64, None) == 1   # x misaligned
+    assert L.gdn_conv1d(1, 10, 0, None, 64, 4, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 1    # varlen w/o cu
+    d = _dims(g)
+    ws = g.workspace_size(d)
+    args = [ctypes.byref(d), 16, 16, 16, 16, 16, None, None, 16, None]
+    assert L.gdn_prefill_chunked(*args, 256, 1024, None) == 3          # workspace too small
+    assert L.gdn_prefill_chunked(*args, 128, ws, None) == 3            # workspace misaligned
+    assert L.gdn_prefill_chunked(ctypes.byref(d), 16, 16, 16, 16, 16, None, None, 0, None, 256, ws, None) == 1
+    assert L.gdn_prefill_chunked(ctypes.byref(d), 16, 16, 8, 16, 16, None, None, 16, None, 256, ws, None) == 1
+    dd = _dims(g, num_seqs=4, total_tokens=4, seqlen=1)
+    assert L.gdn_decode_step(ctypes.byref(dd), 16, 16, 16, 16, 16, 16, 2, None, 16, None) == 1   # slots < B
+    assert L.gdn_decode_step(ctypes.byref(dd), 16, 16, 16, 16, 16, None, 4, None, 16, None) == 1  # no state
+    assert L.gdn_prefill_scan(ctypes.byref(_dims(g, seqlen=0, total_tokens=8, num_seqs=1)), 16, 16, 16, 16, 16,
+                              None, None, 16, None, 256, 1 << 30, None) == 1                    # varlen w/o cu

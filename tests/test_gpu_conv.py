@@ -1,0 +1,116 @@
+"""GPU causal conv1d (+SiLU) through the C ABI against the oracle's fp32
+evaluation: bit-exact outputs and windows."""
+import numpy as np
+import pytest
+
+from linear_attention_delta_amd import synth
+from tests.gpu_util import bits_to_dev, note, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    assert torch.cuda.is_available()
+    from linear_attention_delta_amd import gdn
+    return gdn
+
+
+def _bits(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _oracle_bits(orc, x, w, cu, win, bias, silu, dtype):
+    if dtype == "bf16":
+        return orc.conv1d_f32(x, w, cu, window=win, bias=bias, silu=silu, out_bf16=True)
+    return orc.conv1d_f32(x, w, cu, window=win, bias=bias, silu=silu).view(np.uint32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("width", [2, 4, 5, 8])
+def test_conv_varlen_bitexact(G, orc, dtype, width):
+    import torch
+    note(f"conv varlen dtype={dtype} W={width}")
+    r = np.random.default_rng(width)
+    C = 96 if dtype == "f32" else 160
+    lens = [1, 0, 2, 3, 37, 16, 5, 70]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(cu[-1])
+    x = synth.round_bf16(r.normal(size=(N, C)).astype(np.float32)) if dtype == "bf16" else r.normal(size=(N, C)).astype(np.float32)
+    w = (0.5 * r.normal(size=(C, width))).astype(np.float32)
+    bias = r.normal(size=C).astype(np.float32)
+    win = r.normal(size=(len(lens), width - 1, C)).astype(np.float32)
+    if dtype == "bf16":
+        win = synth.round_bf16(win)
+    for use_win in (False, True):
+        for b in (None, bias):
+            for silu in (True, False):
+                # strided x (rows padded) like a slice of a wider projection
+                xs = torch.zeros((N, C + 16), dtype=torch.float32)
+                xs[:, :C] = torch.from_numpy(x)
+                xd = xs.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()[:, :C]
+                cs = to_dev(win, dtype) if use_win else None
+                y = G.conv1d(xd, to_dev(w), cu_seqlens=torch.from_numpy(cu).cuda(),
+                             bias=to_dev(b) if b is not None else None, conv_state=cs, activation=silu)
+                torch.cuda.synchronize()
+                ref = _oracle_bits(orc, x, w, cu, win if use_win else None, b, silu, dtype)
+                assert np.array_equal(_bits(y), ref), f"conv mismatch win={use_win} bias={b is not None} silu={silu}"
+                if use_win:
+                    _, wref = orc.conv1d(x, w, cu, window=win)
+                    got = to_np(cs)
+                    for i, L in enumerate(lens):
+                        if L == 0:
+                            assert np.array_equal(got[i], win[i])
+                    assert np.array_equal(got, wref.astype(np.float32)), "window update"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_dense_and_step(G, orc, dtype):
+    import torch
+    note(f"conv dense + decode step dtype={dtype}")
+    r = np.random.default_rng(5)
+    B, T, C, W = 3, 33, 64, 4
+    x = r.normal(size=(B * T, C)).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.round_bf16(x)
+    w = (0.5 * r.normal(size=(C, W))).astype(np.float32)
+    cu = (np.arange(B + 1) * T).astype(np.int32)
+    win = r.normal(size=(B, W - 1, C)).astype(np.float32)
+    if dtype == "bf16":
+        win = synth.round_bf16(win)
+    cs = to_dev(win, dtype)
+    y = G.conv1d(to_dev(x, dtype), to_dev(w), seqlen=T, conv_state=cs)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y), _oracle_bits(orc, x, w, cu, win, None, True, dtype))
+    _, wref = orc.conv1d(x, w, cu, window=win)
+    assert np.array_equal(to_np(cs), wref.astype(np.float32))
+    # decode-time step: one token per sequence, window carried
+    win_np = wref.astype(np.float32)
+    for step in range(5):
+        xt = r.normal(size=(B, C)).astype(np.float32)
+        if dtype == "bf16":
+            xt = synth.round_bf16(xt)
+        yt = G.conv1d(to_dev(xt, dtype), to_dev(w), seqlen=1, num_seqs=B, conv_state=cs)
+        torch.cuda.synchronize()
+        cu1 = np.arange(B + 1).astype(np.int32)
+        assert np.array_equal(_bits(yt), _oracle_bits(orc, xt, w, cu1, win_np, None, True, dtype)), f"step {step}"
+        _, win_np = orc.conv1d(xt, w, cu1, window=win_np)
+        win_np = win_np.astype(np.float32)
+        assert np.array_equal(to_np(cs), win_np), f"window after step {step}"
+
+
+def test_conv_qwen35_4k_bitexact(G, orc):
+    """The 4096-token, 8192-channel bf16 layer conv (as the prefill bench runs it)."""
+    import torch
+    inp = synth.prefill_4k_bf16()
+    note(f"conv {inp.name}: {inp.x.shape}")
+    y = G.conv1d(to_dev(inp.x, "bf16"), to_dev(inp.conv_w), seqlen=4096)
+    torch.cuda.synchronize()
+    ref = orc.conv1d_f32(inp.x, inp.conv_w, inp.cu_seqlens, out_bf16=True)
+    got = _bits(y)
+    bad = int(np.sum(got != ref))
+    assert bad == 0, f"{bad} mismatching elements"
