@@ -1,0 +1,307 @@
+"""Benchmark of the Gated DeltaNet layer core on one MI355X.
+
+One step = the prefill path of one layer over the 4096-token workload
+(B=1, T=4096, 16 q/k heads, 32 v heads, d_k=d_v=128, bf16 in, fp32 state,
+chunk 64): the causal conv1d+SiLU over the 8192 projected channels, then
+the chunked prefill (phase 1 + phase 2) producing o and the final state.
+`value` is tokens/s of that step.  Inputs are resident in HBM before timing
+starts; 4 input/output buffer sets (~750 MB) are rotated so the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+The decode path (conv step + recurrent step, B=64, fp32 32x128x128 states,
+4 rotated state pools of 134 MB) is measured in the same run and reported
+under "decode".  Per-kernel times come from HIP events recorded on the
+launch stream around each library call; each call is one kernel.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # dense bf16 matrix
+METRIC = "GDN prefill tokens/s per layer (T=4096) + decode step HBM GB/s, % roofline"
+
+
+def prefill_alg_bytes(T, hk, hv, dk, dv, n_seq=1, esize=2, state_in=False):
+    """Algorithmic bytes of the prefill: q, k, v, o in the input dtype, g and
+    beta in fp32, and the fp32 final state (+ the initial state if read)."""
+    per_tok = (2 * hk * dk + 2 * hv * dv) * esize + 2 * hv * 4
+    st = n_seq * hv * dk * dv * 4
+    return T * per_tok + st * (2 if state_in else 1)
+
+
+def prefill_alg_flops(T, hv, dk, dv, C=64):
+    """Triangular-counted flops of the chunked algorithm: A = K K^T and P = Q K^T
+    (lower triangles), the chunk inverse (C^3/6), W/U products, the three
+    C x d_k x d_v state products and P U."""
+    per_chunk = 2 * (C * (C - 1) / 2 * dk + C * (C + 1) / 2 * dk + C ** 3 / 6
+                     + 2 * C * (C - 1) / 2 * dk + 3 * C * dk * dv + C * (C + 1) / 2 * dv)
+    return per_chunk * (T / C) * hv
+
+
+def conv_alg_bytes(T, C, esize=2, W=4):
+    return T * C * esize * 2 + C * W * 4
+
+
+def decode_alg_bytes(B, hk, hv, dk, dv, esize=2):
+    return 2 * B * hv * dk * dv * 4 + B * (2 * hk * dk + 2 * hv * dv) * esize + 2 * B * hv * 4
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_delta_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=4, help="rotated buffer sets (MALL control)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by "
+              "heads or sequences with no collective inside it); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_delta_amd import gdn, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- prefill
+    inp = synth.prefill_4k_bf16()
+    sh = inp.shape
+    T = inp.total_tokens
+    CC = sh.conv_channels
+    a = sh.num_qk_heads * sh.head_dim_k
+    nsets = max(1, args.sets)
+    w = torch.from_numpy(inp.conv_w).to(dev)
+    sets = []
+    for i in range(nsets):
+        x = torch.from_numpy(inp.x).to(torch.bfloat16).to(dev)
+        y = torch.empty((T, CC), dtype=torch.bfloat16, device=dev)
+        q = y[:, :a].view(T, sh.num_qk_heads, sh.head_dim_k)
+        k = y[:, a:2 * a].view(T, sh.num_qk_heads, sh.head_dim_k)
+        v = y[:, 2 * a:].view(T, sh.num_v_heads, sh.head_dim_v)
+        g = torch.from_numpy(inp.g).to(dev)
+        beta = torch.from_numpy(inp.beta).to(dev)
+        o = torch.empty((T, sh.num_v_heads, sh.head_dim_v), dtype=torch.bfloat16, device=dev)
+        st = torch.empty((1, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v), dtype=torch.float32, device=dev)
+        p = gdn.Prefill(q, k, v, seqlen=T, chunk_size=64)
+        sets.append(dict(x=x, y=y, q=q, k=k, v=v, g=g, beta=beta, o=o, st=st, p=p))
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.conv1d(s["x"], w, seqlen=T, out=s["y"])
+        if ev is not None:
+            ev[1].record(stream)
+        s["p"].prepare(s["q"], s["k"], s["g"], s["beta"])
+        if ev is not None:
+            ev[2].record(stream)
+        s["p"].scan(s["q"], s["k"], s["v"], s["g"], s["beta"], s["o"], None, s["st"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    k_conv = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3   # us
+    k_prep = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    k_scan = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    # warm figure: one buffer set, back to back (MALL may serve it)
+    warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(50)]
+    for i in range(10):
+        step(sets[0])
+    for i in range(50):
+        step(sets[0], warm_evs[i])
+    torch.cuda.synchronize()
+    warm_scan = float(np.mean([e[2].elapsed_time(e[3]) for e in warm_evs]) * 1e3)
+    warm_prep = float(np.mean([e[1].elapsed_time(e[2]) for e in warm_evs]) * 1e3)
+    warm_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in warm_evs]) * 1e3)
+
+    B_pre = prefill_alg_bytes(T, sh.num_qk_heads, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
+    F_pre = prefill_alg_flops(T, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
+    B_conv = conv_alg_bytes(T, CC)
+    kernels = {"conv1d": float(k_conv.mean()), "prefill_prepare": float(k_prep.mean()),
+               "prefill_scan": float(k_scan.mean())}
+    dominant = max(kernels, key=kernels.get)
+    dom_us = kernels[dominant]
+    # the prefill kernels must together move the prefill's algorithmic bytes;
+    # the dominant kernel is charged with the bytes of the call it serves
+    dom_bytes = {"conv1d": B_conv, "prefill_prepare": B_pre, "prefill_scan": B_pre}[dominant]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = read_traffic(dominant)
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "alg_bytes_per_launch": int(dom_bytes),
+                "avg_launch_us": round(dom_us, 2)}
+    pre_us = kernels["prefill_prepare"] + kernels["prefill_scan"]
+
+    # ----------------------------------------------------------------- decode
+    dinp = synth.decode_b64_bf16()
+    dsh = dinp.shape
+    Bd = dinp.batch
+    npool = 4
+    pools = [torch.from_numpy(dinp.state0).to(dev) for _ in range(npool)]
+    cwins = [torch.from_numpy(dinp.conv_state0).to(torch.bfloat16).to(dev) for _ in range(npool)]
+    xs = [torch.from_numpy(dinp.x[p]).to(torch.bfloat16).to(dev) for p in range(dinp.pool)]
+    gs = [torch.from_numpy(dinp.g[p]).to(dev) for p in range(dinp.pool)]
+    bs = [torch.from_numpy(dinp.beta[p]).to(dev) for p in range(dinp.pool)]
+    wd = torch.from_numpy(dinp.conv_w).to(dev)
+    yd = torch.empty((Bd, dsh.conv_channels), dtype=torch.bfloat16, device=dev)
+    od = torch.empty((Bd, dsh.num_v_heads, dsh.head_dim_v), dtype=torch.bfloat16, device=dev)
+    ad = dsh.num_qk_heads * dsh.head_dim_k
+    qd = yd[:, :ad].view(Bd, dsh.num_qk_heads, dsh.head_dim_k)
+    kd = yd[:, ad:2 * ad].view(Bd, dsh.num_qk_heads, dsh.head_dim_k)
+    vd = yd[:, 2 * ad:].view(Bd, dsh.num_v_heads, dsh.head_dim_v)
+
+    def dstep(i, ev=None):
+        p = i % dinp.pool
+        pool = i % npool
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.conv1d(xs[p], wd, seqlen=1, num_seqs=Bd, conv_state=cwins[pool], out=yd)
+        if ev is not None:
+            ev[1].record(stream)
+        gdn.decode_step(qd, kd, vd, gs[p], bs[p], pools[pool], out=od)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(20):
+        dstep(i)
+    torch.cuda.synchronize()
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+    dw0 = time.perf_counter()
+    for i in range(args.decode_steps):
+        dstep(i, devs[i])
+    torch.cuda.synchronize()
+    dwall = time.perf_counter() - dw0
+    d_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]) * 1e3)
+    d_step = float(np.mean([e[1].elapsed_time(e[2]) for e in devs]) * 1e3)
+    B_dec = decode_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v)
+    dec_gbs = B_dec / (d_step * 1e-6) / 1e9
+    decode = {"workload": dinp.name, "batch": Bd, "state_pools": npool, "steps": args.decode_steps,
+              "decode_step_us": round(d_step, 2), "conv_step_us": round(d_conv, 2),
+              "ms_per_token_step_wall": round(dwall * 1e3 / args.decode_steps, 4),
+              "tokens_per_s": round(Bd / (dwall / args.decode_steps), 1),
+              "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": read_traffic("decode_step"), "alg_bytes_per_launch": int(B_dec),
+                           "avg_launch_us": round(d_step, 2)}}
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        y64, _ = oracle.conv1d(inp.x, inp.conv_w)
+        qo, ko, vo = synth.split_qkv(y64, sh)
+        _, _, nt = oracle.scan(qo, ko, vo, inp.g, inp.beta, n_threads=min(16, oracle.available_cores()),
+                               return_threads=True)
+        ct = time.perf_counter() - t0
+        cpu = {"value": round(T / ct, 1), "unit": "tokens/s", "cores": int(nt), "kind": "oracle",
+               "sample": f"whole workload once: fp64 conv1d+SiLU over {T}x{CC} and the token-by-token "
+                         f"scan of all {sh.num_v_heads} v-heads x {T} tokens, {ct:.2f} s on {cpu_model()}"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Qwen3.5-4B-shaped GDN layer)",
+        "config": {"workload": inp.name, "global_batch": 1, "seq_len": T, "qk_heads": sh.num_qk_heads,
+                   "v_heads": sh.num_v_heads, "head_dim": sh.head_dim_k, "chunk": 64, "conv_width": 4,
+                   "step": "conv1d+SiLU -> prefill prepare -> prefill scan", "buffer_sets": nsets},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v, 2) for k, v in kernels.items()},
+        "gpu_ms_per_step_events": round(gpu_ms / args.steps, 5),
+        "prefill_only": {"us": round(pre_us, 2), "tokens_per_s": round(T / (pre_us * 1e-6), 1),
+                         "hbm_frac": round(B_pre / (pre_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_frac_bf16": round(F_pre / (pre_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "alg_bytes": int(B_pre), "alg_flops": int(F_pre)},
+        "warm_single_set_us": {"conv1d": round(warm_conv, 2), "prefill_prepare": round(warm_prep, 2),
+                               "prefill_scan": round(warm_scan, 2)},
+        "decode": decode,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,8 +137,10 @@ gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen,
 
 /*
  * Device workspace (bytes) that gdn_prefill_chunked / gdn_prefill_prepare /
- * gdn_prefill_scan need for this problem: the per-chunk inverses and the
- * chunk table.  0 on invalid dims (gdn_last_error says why).
+ * gdn_prefill_scan need for this problem: per chunk and v-head the inverse
+ * Tt, the score matrix P (both C x C in the q/k/v dtype) and four C-vectors
+ * of fp32 scale factors, plus the chunk table for varlen input.  0 on invalid
+ * dims (gdn_last_error says why).
  */
 size_t gdn_prefill_workspace_size(const gdn_dims *d);
 
@@ -171,12 +173,15 @@ gdn_status gdn_prefill_chunked(const gdn_dims *d, const void *q, const void *k,
  * Phase 1 of the prefill: everything that does not depend on the carried
  * state (the oxydllm notes, "Performance": the cross-chunk loop precomputes
  * all state-independent work in batch).  For every chunk and v-head it
- * writes Tinv(I + A) diag(beta) into the workspace; fully parallel over
- * chunks.  Arguments as gdn_prefill_chunked.
+ * writes into the workspace Tt = (I + A)^{-1} diag(beta), the causal score
+ * matrix P[r][s] = e^{gamma_r - gamma_s} q_hat_r . k_hat_s (s <= r) and the
+ * per-token scale factors; fully parallel over chunks.  Arguments as
+ * gdn_prefill_chunked.
  */
-gdn_status gdn_prefill_prepare(const gdn_dims *d, const void *k, const float *g,
-                               const float *beta, const int32_t *cu_seqlens,
-                               void *workspace, size_t ws_bytes, void *stream);
+gdn_status gdn_prefill_prepare(const gdn_dims *d, const void *q, const void *k,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, void *workspace,
+                               size_t ws_bytes, void *stream);
 
 /*
  * Phase 2 of the prefill: the sequential carry over chunks, reading the

@@ -101,6 +101,28 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
     seq_end = a.cu_seqlens[seq + 1];
   }
 
+  // Fast path: the block and its W-1 token halo lie inside one sequence.
+  // Issue all TOK + W - 1 row loads at once, then compute.
+  if (t_end - t_begin == TOK && t_begin - (W - 1) >= seq_start && t_end <= seq_end) {
+    float rows[TOK + W - 1][V];
+#pragma unroll
+    for (int j = 0; j < TOK + W - 1; j++) Vec<E>::load(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0, rows[j]);
+#pragma unroll
+    for (int tt = 0; tt < TOK; tt++) {
+      float out[V];
+#pragma unroll
+      for (int i = 0; i < V; i++) {
+        float acc = bias[i];
+#pragma unroll
+        for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], rows[tt + j][i], acc);
+        out[i] = a.activation ? silu_exact(acc) : acc;
+      }
+      Vec<E>::store(y + (long)(t_begin + tt) * a.stride_y + c0, out);
+    }
+    return;
+  }
+
+  // General path (sequence starts inside the block): walk token by token.
   // hist[j] = input at position t - (W-1) + j for the token t about to run
   float hist[W][V];
   auto fill_context = [&](int t) {

@@ -101,17 +101,25 @@ int64_t max_chunks(const gdn_dims* d) {
   return (int64_t)d->total_tokens / C + d->num_seqs;
 }
 
+// Workspace: [chunk table (varlen only)] [Tt, P per chunk and v-head]
+// [a, b, c, e^{gamma_last} per chunk and v-head], each part 256-byte aligned.
 struct WsLayout {
-  size_t table_off, table_bytes, tinv_off, tinv_bytes, total;
+  size_t table_off, table_bytes, mats_off, mats_bytes, scal_off, scal_bytes, total;
 };
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 WsLayout ws_layout(const gdn_dims* d) {
   WsLayout w;
+  const size_t units = (size_t)max_chunks(d) * d->num_v_heads;
+  const size_t C = d->chunk_size;
   w.table_off = 0;
-  w.table_bytes = d->seqlen > 0 ? 0 : (((size_t)(d->num_seqs + 1) * 4 + 255) / 256) * 256;
-  w.tinv_off = w.table_bytes;
-  w.tinv_bytes = (size_t)max_chunks(d) * d->num_v_heads * d->chunk_size * d->chunk_size * elem_size(d->dtype);
-  w.total = w.tinv_off + w.tinv_bytes;
+  w.table_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1) * 4);
+  w.mats_off = w.table_bytes;
+  w.mats_bytes = align256(units * 2 * C * C * elem_size(d->dtype));
+  w.scal_off = w.mats_off + w.mats_bytes;
+  w.scal_bytes = align256(units * 4 * C * 4);
+  w.total = w.scal_off + w.scal_bytes;
   return w;
 }
 
@@ -184,7 +192,8 @@ void carve(gdn::ScanArgs& a, const gdn_dims* d, const void* ws) {
   const WsLayout L = ws_layout(d);
   char* base = reinterpret_cast<char*>(const_cast<void*>(ws));
   a.chunk_offsets = L.table_bytes ? reinterpret_cast<int32_t*>(base + L.table_off) : nullptr;
-  a.tinv = base ? base + L.tinv_off : nullptr;
+  a.tinv = base ? base + L.mats_off : nullptr;
+  a.scal = base ? reinterpret_cast<float*>(base + L.scal_off) : nullptr;
   a.max_chunks = (int)max_chunks(d);
 }
 
@@ -283,13 +292,15 @@ size_t gdn_prefill_workspace_size(const gdn_dims* d) {
   return ws_layout(d).total;
 }
 
-gdn_status gdn_prefill_prepare(const gdn_dims* d, const void* k, const float* g, const float* beta,
+gdn_status gdn_prefill_prepare(const gdn_dims* d, const void* q, const void* k, const float* g, const float* beta,
                                const int32_t* cu_seqlens, void* workspace, size_t ws_bytes, void* stream) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
-  if ((st = check_scan_ptrs(d, nullptr, k, nullptr, g, beta, cu_seqlens, false)) != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, nullptr, g, beta, cu_seqlens, false)) != GDN_OK) return st;
+  if (d->total_tokens > 0 && (!q || !aligned(q, 16))) return fail(GDN_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
   if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
   gdn::ScanArgs a = make_args(d);
+  a.q = q;
   a.k = k;
   a.g = g;
   a.beta = beta;
@@ -344,7 +355,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, 
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
     return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
-  if ((st = gdn_prefill_prepare(d, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
+  if ((st = gdn_prefill_prepare(d, q, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
   return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
 }
 

@@ -41,6 +41,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two fp32 -> packed bf16 pair with the gfx950 convert instruction (round to
+// nearest even).  Used on the tolerance-checked paths; the bit-exact
+// convolution keeps its own rounding above.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Element traits: storage type of q/k/v/o and of the MFMA operands.
 struct BF16 {
   typedef uint16_t store_t;
@@ -92,6 +102,20 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const typename E::store_t* 
 }
 
 // ---------------------------------------------------------- reductions
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32 or 64), every lane
+// of a group receiving the group's sum.  Within 16-lane rows the exchange
+// uses DPP lane swizzles (no LDS traffic).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += __builtin_amdgcn_update_dpp(0.f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if (N >= 4) v += __builtin_amdgcn_update_dpp(0.f, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if (N >= 8) v += __builtin_amdgcn_update_dpp(0.f, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if (N >= 16) v += __builtin_amdgcn_update_dpp(0.f, v, 0x140, 0xF, 0xF, false); // row_mirror
+  if (N >= 32) v += __shfl_xor(v, 16, 64);
+  if (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

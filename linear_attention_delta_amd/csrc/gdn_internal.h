@@ -40,7 +40,8 @@ struct ScanArgs {
   float* state_out;
   // workspace carve-up
   int32_t* chunk_offsets;     // [num_seqs + 1], varlen only
-  void* tinv;                 // [max_chunks][hv][chunk][chunk] in the operand type
+  void* tinv;                 // [max_chunks][hv][2][chunk][chunk] in the operand type: Tt, P
+  float* scal;                // [max_chunks][hv][4][chunk] fp32: a, b, c, e^{gamma_last}
   int max_chunks;
   // decode only
   float* state;

@@ -4,29 +4,30 @@
 // runtime; "Performance", Gated DeltaNet fast paths) run prefill as a chunked
 // parallel scan: the state-independent work of every chunk is done in batch,
 // then a sequential loop carries the state across chunks.  For a chunk of C
-// tokens (gamma_r = g_0 + ... + g_r inside the chunk, k_hat = rk k, q_hat = rq q):
+// tokens (gamma_r = g_0 + ... + g_r inside the chunk, k_hat = rk k,
+// q_hat = rq q, rk = 1/|k|, rq = scale/|q|):
 //
 //   A[r,s] = beta_r e^{gamma_r - gamma_s} k_hat_r . k_hat_s     (s < r)
 //   Tt     = (I + A)^{-1} diag(beta)
-//   U      = Tt (V - diag(e^gamma) K_hat S)                 -- new values
 //   P[r,s] = e^{gamma_r - gamma_s} q_hat_r . k_hat_s          (s <= r)
-//   O      = diag(e^gamma) Q_hat S + P U
-//   S     <- e^{gamma_last} S + K_hat^T diag(e^{gamma_last - gamma}) U
+//   a_r = e^{gamma_r} rk_r,  b_r = e^{gamma_r} rq_r,  c_r = e^{gamma_last - gamma_r} rk_r
 //
-// Phase 1 (k_prepare): one workgroup per (chunk, v-head) builds A from
-// K K^T on the matrix cores and inverts I + A blockwise -- the doubling
-// product (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8) on each 16x16 diagonal
-// block (N^16 = 0), then pairwise merging 16 -> 32 -> 64 with
+//   U  = Tt (V - diag(a) K S)                                -- new values
+//   O  = diag(b) Q S + P U
+//   S <- e^{gamma_last} S + K^T diag(c) U
+//
+// Phase 1 (k_prepare): one workgroup per (chunk, v-head), fully parallel.
+// It forms K K^T and K Q^T on the matrix cores, inverts I + A blockwise --
+// the doubling product (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8) on each 16x16
+// diagonal block (N^16 = 0), then pairwise merging 16 -> 32 -> 64 with
 // [[X,0],[Y,Z]]^{-1} = [[X^-1,0],[-Z^-1 Y X^-1, Z^-1]] -- never powers of the
 // whole 64x64 block, which overflow fp32 on repeated tokens (the notes'
-// failure of plain doubling at chunk 64).  It writes Tt to the workspace.
+// failure of plain doubling at chunk 64) -- and writes Tt, P and a, b, c,
+// e^{gamma_last} to the workspace.
 //
-// Phase 2 (k_scan): one workgroup per (sequence, v-head, 16 columns of d_v)
-// walks the chunks in order with its 128x16 fp32 slice of S in registers.
-// Each chunk it stages K, Q, V and Tt in LDS, forms P on the matrix cores
-// (state independent, so it overlaps the dependent chain), then runs the
-// chain X = K S -> U -> (O, S).  Only Tt crosses HBM between the phases;
-// P, U and the per-chunk states never leave the chip.
+// Phase 2 (k_scan): one workgroup per (sequence, v-head, NT*16 columns of
+// d_v) walks the chunks in order with its d_k x NT*16 fp32 slice of S in
+// registers; per chunk only the four state-dependent products remain.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -130,93 +131,135 @@ __device__ __forceinline__ void st16_plus_i(float* D, int ldd, f32x4 v, int lane
 
 // ---------------------------------------------------------------- phase 1
 
+// Workspace block of one (chunk, v-head): Tt [C][C] then P [C][C] in the
+// operand type, and (separately) 4 x C fp32 scalars: a, b, c and
+// e^{gamma_last} (first element of the fourth row).
 template <class E, int C, int DK>
 struct alignas(16) PrepSmem {
   typedef typename E::store_t T;
   static constexpr int KLD = DK + 16 / sizeof(T);  // row pad: 16 bytes
-  static constexpr int ALD = C + 1;
+  static constexpr int ALD = C + 4;                // 16-byte aligned rows
   static constexpr int SLD = 17;
   T k[C][KLD];
+  T q[C][KLD];
   float at[C][ALD];            // A, then (I + A)^{-1} in place
   float sc[4][4][16][SLD];     // per-wave 16x16 scratch
   float w1[32][33];
-  float gam[C], bet[C], rk[C];
+  float gam[C], bet[C], rk[C], rq[C];
 };
 
 template <class E, int C, int DK>
 __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   typedef typename E::store_t T;
   typedef PrepSmem<E, C, DK> SM;
+  constexpr int NRT = C / 16;
   __shared__ SM sm;
   const int h = blockIdx.y;
   int seq, start, len;
   if (!chunk_of(a, C, blockIdx.x, seq, start, len)) return;
   const int hk = a.tiled ? (h % a.hk) : (h / (a.hv / a.hk));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
-  // ---- stage K rows (zero past the end of the sequence), g, beta
+  // ---- stage K and Q rows (zero past the end of the sequence); all loads
+  // are issued before any is used.  Row norms come from the registers.
   {
-    constexpr int VPR = DK * sizeof(T) / 16;  // 16-byte vectors per row
+    constexpr int EPV = 16 / sizeof(T);
+    constexpr int VPR = DK / EPV;  // 16-byte vectors per row
+    constexpr int NV = 2 * C * VPR / 256;
+    static_assert(NV * 256 == 2 * C * VPR, "K/Q staging must tile the workgroup");
     const T* kp = reinterpret_cast<const T*>(a.k);
-    for (int idx = tid; idx < C * VPR; idx += 256) {
-      const int r = idx / VPR, cv = idx % VPR;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (r < len)
-        w = *reinterpret_cast<const u32x4*>(kp + (long)(start + r) * a.stride_k + (long)hk * DK + cv * (16 / sizeof(T)));
-      *reinterpret_cast<u32x4*>(&sm.k[r][cv * (16 / sizeof(T))]) = w;
+    const T* qp = reinterpret_cast<const T*>(a.q);
+    u32x4 w[NV];
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + 256 * j;
+      const int which = idx / (C * VPR);
+      const int rem = idx % (C * VPR);
+      const int r = rem / VPR, cv = rem % VPR;
+      w[j] = u32x4{0u, 0u, 0u, 0u};
+      if (r < len) {
+        const T* src = which ? qp + (long)(start + r) * a.stride_q : kp + (long)(start + r) * a.stride_k;
+        w[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
+      }
     }
-  }
-  if (wave == 0) {
     float gv = 0.f, bv = 0.f;
-    if (lane < len) {
+    if (wave == 0 && lane < len) {
       gv = a.g[(long)(start + lane) * a.hv + h];
       bv = a.beta[(long)(start + lane) * a.hv + h];
     }
-    const float gm = wave_prefix_sum(gv, lane);
-    if (lane < C) {
-      sm.gam[lane] = gm;
-      sm.bet[lane] = bv;
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + 256 * j;
+      const int which = idx / (C * VPR);
+      const int rem = idx % (C * VPR);
+      const int r = rem / VPR, cv = rem % VPR;
+      *reinterpret_cast<u32x4*>(which ? &sm.q[r][cv * EPV] : &sm.k[r][cv * EPV]) = w[j];
+      const T* e = reinterpret_cast<const T*>(&w[j]);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPV; i++) {
+        const float x = E::to_f32(e[i]);
+        ss += x * x;
+      }
+      ss = group_sum<VPR>(ss);
+      if (cv == 0) {
+        const float inv = a.l2norm ? __builtin_amdgcn_rsqf(ss + kL2Eps) : 1.0f;
+        if (which) sm.rq[r] = a.scale * inv; else sm.rk[r] = inv;
+      }
+    }
+    if (wave == 0) {
+      const float gm = wave_prefix_sum(gv, lane);
+      if (lane < C) {
+        sm.gam[lane] = gm;
+        sm.bet[lane] = bv;
+      }
     }
   }
   __syncthreads();
-  // ---- row norms of K
+  // ---- transposed Gram tiles D[s][r] = k_s . x_r (x = k or q), s-block j,
+  // r-block i: each lane then owns 4 consecutive s of one row r.
+  //   A[r][s] = beta_r rk_r rk_s e^{gamma_r - gamma_s} k_r.k_s  (s < r)  -> LDS
+  //   P[r][s] = rq_r rk_s e^{gamma_r - gamma_s} q_r.k_s         (s <= r) -> workspace
   {
-    constexpr int TPR = 256 / C;  // threads per row
-    constexpr int EPT = DK / TPR;
-    const int r = tid / TPR, part = tid % TPR;
-    float ss = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < EPT; i++) {
-      const float x = E::to_f32(sm.k[r][part * EPT + i]);
-      ss += x * x;
-    }
+    T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + h) * (2 * C * C) + C * C;
+    for (int t = wave; t < 2 * NRT * NRT; t += 4) {
+      const int which = t / (NRT * NRT);  // 0: A, 1: P
+      const int i = (t % (NRT * NRT)) / NRT, j = t % NRT;
+      const int r = 16 * i + c16, s0 = 16 * j + r4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (j <= i) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = tile_mma<E, DK>(acc, &sm.k[16 * j][0], SM::KLD, which ? &sm.q[16 * i][0] : &sm.k[16 * i][0],
+                              SM::KLD, lane);
+        const float gr = sm.gam[r];
+        const float fr = which ? sm.rq[r] : sm.bet[r] * sm.rk[r];
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-    if (part == 0) sm.rk[r] = a.l2norm ? 1.0f / sqrtf(ss + kL2Eps) : 1.0f;
+        for (int e = 0; e < 4; e++) {
+          const int s = s0 + e;
+          const bool keep = which ? (s <= r) : (s < r);
+          v[e] = keep ? fr * sm.rk[s] * __expf(gr - sm.gam[s]) * acc[e] : 0.f;
+        }
+      }
+      if (which == 0) {
+        *reinterpret_cast<f32x4*>(&sm.at[r][s0]) = v;
+      } else if constexpr (std::is_same<E, BF16>::value) {
+        u32x2 w2 = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(pout + r * C + s0) = w2;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(pout) + r * C + s0) = v;
+      }
+    }
   }
-  __syncthreads();
-  // ---- A = strict lower part of diag(beta) (decay * K_hat K_hat^T)
-  {
-    constexpr int NT = C / 16;
-    for (int t = wave; t < NT * NT; t += 4) {
-      const int i = t / NT, j = t % NT;
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
-      if (j > i) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) sm.at[16 * i + r0 + e][16 * j + c] = 0.f;
-        continue;
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile_mma<E, DK>(acc, &sm.k[16 * i][0], SM::KLD, &sm.k[16 * j][0], SM::KLD, lane);
-      const int s = 16 * j + c;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 16 * i + r0 + e;
-        float v = 0.f;
-        if (s < r) v = sm.bet[r] * sm.rk[r] * sm.rk[s] * __expf(sm.gam[r] - sm.gam[s]) * acc[e];
-        sm.at[r][s] = v;
-      }
-    }
+  // ---- per-token scalars a, b, c and e^{gamma_last}
+  if (wave == 1 && lane < C) {
+    float* scal = a.scal + ((long)blockIdx.x * a.hv + h) * (4 * C);
+    const float gm = sm.gam[lane], glast = sm.gam[C - 1];
+    const float eg = __expf(gm);
+    scal[lane] = eg * sm.rk[lane];
+    scal[C + lane] = eg * sm.rq[lane];
+    scal[2 * C + lane] = __expf(glast - gm) * sm.rk[lane];
+    scal[3 * C + lane] = lane == 0 ? __expf(glast) : 0.f;
   }
   __syncthreads();
   // ---- 16x16 diagonal blocks: (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8)
@@ -238,9 +281,8 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
     st16_plus_i(s0, S, n2, lane);  // I + N^2
     st16_plus_i(s1, S, n4, lane);  // I + N^4
     {  // I - N
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
 #pragma unroll
-      for (int e = 0; e < 4; e++) s3[(r0 + e) * S + c] = (r0 + e == c ? 1.f : 0.f) - N[(r0 + e) * L + c];
+      for (int e = 0; e < 4; e++) s3[(r4 + e) * S + c16] = (r4 + e == c16 ? 1.f : 0.f) - N[(r4 + e) * L + c16];
     }
     wave_lds_sync();
     f32x4 p = mm16_f32<16>(s3, S, s0, S, lane);
@@ -293,39 +335,55 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   __syncthreads();
   // ---- Tt = inv diag(beta), upper triangle zero, to the workspace
   {
-    T* out = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + h) * (C * C);
-    for (int idx = tid; idx < C * C; idx += 256) {
-      const int r = idx / C, s = idx % C;
-      const float v = s <= r ? sm.at[r][s] * sm.bet[s] : 0.f;
-      out[idx] = E::from_f32(v);
+    T* out = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + h) * (2 * C * C);
+    for (int idx = tid; idx < C * C / 4; idx += 256) {
+      const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.at[r][s0]);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * sm.bet[s0 + e] : 0.f;
+      if constexpr (std::is_same<E, BF16>::value) {
+        u32x2 w2 = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(out + r * C + s0) = w2;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + r * C + s0) = v;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- phase 2
+//
+// One workgroup per (sequence, v-head, NT*16 columns of d_v), 4*NT waves.
+// Waves 4t..4t+3 own column tile t; within it wave lw owns token rows
+// 16lw..16lw+15 of the chunk (X, U, O) and d_k rows of the state (S).
+// Per chunk (staged data in LDS buffer b, the next chunk's loads in flight):
+//   B0 | X = K S -> R | B1 | U = Tt R | B2 | O^T = diag(b) S^T Q^T + U^T P^T ;
+//        S <- e^{gl} S + K^T diag(c) U ; stage next chunk
+// O is formed transposed so each lane owns 4 consecutive columns of one
+// token row and writes them with one 8- or 16-byte store.
 
-template <class E, int C, int DK>
+template <class E, int C, int DK, int NT, bool DB>
 struct alignas(16) ScanSmem {
   typedef typename E::store_t T;
-  static constexpr bool KT = std::is_same<E, BF16>::value;  // keep K^T for the S update
+  static constexpr int NB = DB ? 2 : 1;            // staging buffers
   static constexpr int PADE = 16 / sizeof(T);
   static constexpr int KLD = DK + PADE;
-  // arrays indexed by token along the MFMA K dimension are padded to a whole
-  // K step (bf16 chunk 16 -> 32 columns); the padding stays zero
+  // token-indexed arrays along the MFMA K dimension are padded to a whole
+  // K step (bf16 chunk 16 -> 32); the padding stays zero
   static constexpr int CW = C > E::KSTEP ? C : E::KSTEP;
   static constexpr int CLD = CW + PADE;
-  T k[C][KLD];
-  T kt[KT ? DK : 1][CLD];
-  T q[C][KLD];
-  T tt[C][CLD];
-  T p[C][CLD];
-  T st[16][KLD];     // S^T (16 columns of d_v x d_k) as operand
-  T rt[16][CLD];     // R^T
-  T ut[16][CLD];     // U^T
-  T u2t[16][CLD];    // (diag(e^{gl - gamma} rk) U)^T
-  float v[C][16];
-  float rk[C], rq[C], gam[C], eg[C], egc[C];
-  float gl;
+  static constexpr int VLD = C + 4;
+  T k[NB][C][KLD];
+  T q[NB][C][KLD];
+  T tt[NB][C][CLD];
+  T p[NB][C][CLD];
+  float vt[NB][16 * NT][VLD];  // V^T slice, fp32
+  float sc[NB][4][C];          // a, b, c, e^{gamma_last}
+  T st[2][NT][16][KLD];        // S^T as operand, double-buffered
+  T rt[NT][16][CLD];           // R^T
+  T ut[NT][16][CLD];           // U^T
+  T u2t[NT][16][CLD];          // (diag(c) U)^T
 };
 
 // D += A B where A(16 x K) = M^T for M row-major [K][ld] (fp32 operands).
@@ -338,6 +396,28 @@ __device__ __forceinline__ f32x4 tile_mma_at_f32(f32x4 acc, const float* M, int 
   return acc;
 }
 
+// D += A B with A(16 x CW) = K^T rows rb..rb+15, K row-major [C][ldk] bf16:
+// each lane gathers its 8 consecutive tokens of one column from LDS.  Tokens
+// at or past C (K-step padding) read as zero.
+template <int C, int LDK, int CW>
+__device__ __forceinline__ f32x4 tile_mma_kt_bf16(f32x4 acc, const uint16_t* K, int rb, const uint16_t* BT, int ldb,
+                                                  int lane) {
+  const int r = lane & 15, kq = (lane >> 4) * 8;
+#pragma unroll
+  for (int kb = 0; kb < CW; kb += 32) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int s0 = kb + kq + 2 * e;
+      const uint32_t lo = (s0 < C) ? K[s0 * LDK + rb + r] : 0u;
+      const uint32_t hi = (s0 + 1 < C) ? K[(s0 + 1) * LDK + rb + r] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    acc = mfma16(__builtin_bit_cast(bf16x8, w), load_frag(BT + r * ldb + kq + kb, BF16()), acc);
+  }
+  return acc;
+}
+
 template <class E>
 __device__ __forceinline__ f32x4 tile_mma_rt(f32x4 acc, const typename E::store_t* A, int lda,
                                              const typename E::store_t* BT, int ldb, int lane, int kend) {
@@ -347,44 +427,50 @@ __device__ __forceinline__ f32x4 tile_mma_rt(f32x4 acc, const typename E::store_
   return acc;
 }
 
-// Write 4 consecutive values of one column into a transposed [16][ld] array.
-__device__ __forceinline__ void st_col4(uint16_t* p, f32x4 v) {
-  u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+// Store 4 consecutive values (one lane's accumulator column) contiguously.
+__device__ __forceinline__ void st4(uint16_t* p, f32x4 v) {
+  u32x2 w = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
   *reinterpret_cast<u32x2*>(p) = w;
 }
-__device__ __forceinline__ void st_col4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-template <class E, int C, int DK>
-__global__ void __launch_bounds__(256) k_scan(ScanArgs a) {
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+template <class E, int C, int DK, int NT, bool DB>
+__global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   typedef typename E::store_t T;
-  typedef ScanSmem<E, C, DK> SM;
+  typedef ScanSmem<E, C, DK, NT, DB> SM;
+  constexpr int NTH = 256 * NT;    // threads
   constexpr int NRT = C / 16;      // 16-row tiles per chunk
-  constexpr int STW = DK / 64;     // S tiles (16 rows) per wave
+  constexpr int STW = DK / 64;     // state row tiles per wave (per column tile)
+  constexpr int KLD = SM::KLD, CLD = SM::CLD;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Zero all staging memory once: the upper triangle of P and the K-step
-  // padding are read by the matrix cores but never written.
+  const int tw = wave >> 2, lw = wave & 3;   // column tile, wave within it
+  const int c16 = lane & 15, r4 = (lane >> 4) * 4;
+
+  // Zero all LDS once: the upper triangles and the K-step padding are read
+  // by the matrix cores but never written.
   {
     u32x4* z = reinterpret_cast<u32x4*>(&sm);
-    for (int i = tid; i < (int)(sizeof(SM) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    for (int i = tid; i < (int)(sizeof(SM) / 16); i += NTH) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- which (sequence, v-head, column tile): XCD-aware numbering.  All
+  // ---- which (sequence, v-head, column block): XCD-aware numbering.  All
   // workgroups reading the same q/k head get the same (id % 8), i.e. the
   // same XCD and L2, since workgroups are dealt round-robin over the 8 XCDs.
-  const int ntiles = a.dv / 16;
+  const int nblk = a.dv / (16 * NT);
   const int G = a.hv / a.hk;
-  const int GS = G * ntiles;                 // workgroups per (seq, qk head)
+  const int GS = G * nblk;                   // workgroups per (seq, qk head)
   const int ngroups = a.num_seqs * a.hk;
   const int xcd = blockIdx.x & 7, m = blockIdx.x >> 3;
   const int grp = (m / GS) * 8 + xcd;
   if (grp >= ngroups) return;
   const int local = m % GS;
   const int seq = grp / a.hk, hk = grp % a.hk;
-  const int vh = local / ntiles;             // which of the G v-heads
+  const int vh = local / nblk;
   const int h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
-  const int dv0 = (local % ntiles) * 16;
+  const int dv0 = (local % nblk) * 16 * NT;
 
   int s0, s1, cbase;
   if (a.seqlen > 0) {
@@ -398,197 +484,177 @@ __global__ void __launch_bounds__(256) k_scan(ScanArgs a) {
   }
   const int nchunks = (s1 - s0 + C - 1) / C;
 
-  // ---- initial state slice: wave w owns rows [w*DK/4, (w+1)*DK/4)
+  __syncthreads();  // zeroing done
+
+  // ---- initial state: wave (tw, lw) owns rows [lw*DK/4, (lw+1)*DK/4) of tile tw
   f32x4 S[STW];
   {
-    const int c = lane & 15, r0 = (lane >> 4) * 4;
     const float* sin = a.state_in ? a.state_in + ((long)seq * a.hv + h) * DK * a.dv : nullptr;
+    const int col = dv0 + 16 * tw + c16;
 #pragma unroll
     for (int t = 0; t < STW; t++) {
-      const int rb = (wave * STW + t) * 16;
+      const int rb = (lw * STW + t) * 16;
 #pragma unroll
-      for (int e = 0; e < 4; e++) S[t][e] = sin ? sin[(long)(rb + r0 + e) * a.dv + dv0 + c] : 0.f;
-      st_col4(&sm.st[c][rb + r0], S[t]);
+      for (int e = 0; e < 4; e++) S[t][e] = sin ? sin[(long)(rb + r4 + e) * a.dv + col] : 0.f;
+      st4(&sm.st[0][tw][c16][rb + r4], S[t]);
     }
   }
 
+  // ---- staging: all global loads of a chunk are issued at once into
+  // registers one chunk ahead (per-thread source pointers are fixed; only a
+  // per-chunk offset moves), then written to LDS.
+  constexpr int EPV = 16 / sizeof(T);              // elements per 16-byte vector
+  constexpr int VPR = DK / EPV;                    // vectors per K/Q row
+  constexpr int KQ_V = 2 * C * VPR;                // K and Q vectors per chunk
+  constexpr int NKQ = (KQ_V + NTH - 1) / NTH;
+  constexpr int M_V = 2 * C * C / EPV;             // Tt and P vectors per chunk
+  constexpr int NM = (M_V + NTH - 1) / NTH;
+  constexpr int V_VPR = 16 * NT / EPV;             // V vectors per row
+  constexpr int V_V = C * V_VPR;
+  constexpr int S_V = C;                           // 4*C scalars = C vectors
+  static_assert(V_V <= NTH && S_V <= NTH, "staging");
   const T* qp = reinterpret_cast<const T*>(a.q);
   const T* kp = reinterpret_cast<const T*>(a.k);
   const T* vp = reinterpret_cast<const T*>(a.v);
-  T* op = reinterpret_cast<T*>(a.o);
-  const T* tp = reinterpret_cast<const T*>(a.tinv);
+  const T* mp = reinterpret_cast<const T*>(a.tinv);
+  const float* scp = a.scal;
+  u32x4 pkq[NKQ], pm[NM], pv = {0u, 0u, 0u, 0u}, ps = {0u, 0u, 0u, 0u};
 
-  for (int ch = 0; ch < nchunks; ch++) {
+  auto load_chunk = [&](int ch) {
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
-    __syncthreads();  // previous chunk finished with the staging buffers
-    // ---- stage K, Q (+K^T), V slice, Tt; zero rows past the end
-    {
-      constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
-      constexpr int VPR = DK / EPV;
-      for (int idx = tid; idx < 2 * C * VPR; idx += 256) {
-        const int which = idx / (C * VPR);  // 0: K, 1: Q
-        const int rem = idx % (C * VPR);
-        const int r = rem / VPR, cv = rem % VPR;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (r < clen) {
-          const T* src = which ? qp + (long)(cs + r) * a.stride_q : kp + (long)(cs + r) * a.stride_k;
-          w = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
-        }
-        T* dst = which ? &sm.q[r][cv * EPV] : &sm.k[r][cv * EPV];
-        *reinterpret_cast<u32x4*>(dst) = w;
-        if (SM::KT && which == 0) {
-          const T* e8 = reinterpret_cast<const T*>(&w);
 #pragma unroll
-          for (int e = 0; e < EPV; e++) sm.kt[SM::KT ? cv * EPV + e : 0][r] = e8[e];
-        }
-      }
-      // Tt: C x C
-      const T* tsrc = tp + ((long)(cbase + ch) * a.hv + h) * (C * C);
-      for (int idx = tid; idx < C * C / EPV; idx += 256) {
-        const int r = idx / (C / EPV), cv = idx % (C / EPV);
-        *reinterpret_cast<u32x4*>(&sm.tt[r][cv * EPV]) = *reinterpret_cast<const u32x4*>(tsrc + idx * EPV);
-      }
-      // V slice: C x 16
-      for (int idx = tid; idx < C * 16; idx += 256) {
-        const int r = idx / 16, c = idx % 16;
-        sm.v[r][c] = r < clen ? E::to_f32(vp[(long)(cs + r) * a.stride_v + (long)h * a.dv + dv0 + c]) : 0.f;
-      }
-      if (wave == 0) {
-        const float gv = lane < clen ? a.g[(long)(cs + lane) * a.hv + h] : 0.f;
-        const float gm = wave_prefix_sum(gv, lane);
-        const float glast = __shfl(gm, C - 1, 64);
-        if (lane < C) {
-          sm.gam[lane] = gm;
-          sm.eg[lane] = __expf(gm);
-          sm.egc[lane] = __expf(glast - gm);
-        }
-        if (lane == 0) sm.gl = __expf(glast);
+    for (int j = 0; j < NKQ; j++) {
+      const int idx = tid + NTH * j;
+      const int which = idx / (C * VPR);  // 0: K, 1: Q
+      const int rem = idx % (C * VPR);
+      const int r = rem / VPR, cv = rem % VPR;
+      pkq[j] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < KQ_V && r < clen) {
+        const T* src = which ? qp + (long)(cs + r) * a.stride_q : kp + (long)(cs + r) * a.stride_k;
+        pkq[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
       }
     }
-    __syncthreads();
-    // ---- row norms of K and Q
-    {
-      constexpr int TPR = 128 / C;
-      constexpr int EPT = DK / TPR;
-      const int which = tid >> 7;  // 0: K, 1: Q
-      const int r = (tid & 127) / TPR, part = (tid & 127) % TPR;
-      const T* row = which ? &sm.q[r][part * EPT] : &sm.k[r][part * EPT];
-      float ss = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < EPT; i++) {
-        const float x = E::to_f32(row[i]);
-        ss += x * x;
-      }
+    const long blk = (long)(cbase + ch) * a.hv + h;
+    const T* msrc = mp + blk * (2 * C * C);
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-      if (part == 0) {
-        const float inv = a.l2norm ? 1.0f / sqrtf(ss + kL2Eps) : 1.0f;
-        if (which) sm.rq[r] = a.scale * inv; else sm.rk[r] = inv;
+    for (int j = 0; j < NM; j++) {
+      const int idx = tid + NTH * j;
+      if (idx < M_V) pm[j] = *reinterpret_cast<const u32x4*>(msrc + idx * EPV);
+    }
+    if (tid < V_V) {
+      const int r = tid / V_VPR, cv = tid % V_VPR;
+      pv = u32x4{0u, 0u, 0u, 0u};
+      if (r < clen)
+        pv = *reinterpret_cast<const u32x4*>(vp + (long)(cs + r) * a.stride_v + (long)h * a.dv + dv0 + cv * EPV);
+    }
+    if (tid < S_V) ps = *reinterpret_cast<const u32x4*>(scp + blk * (4 * C) + tid * 4);
+  };
+
+  auto store_chunk = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < NKQ; j++) {
+      const int idx = tid + NTH * j;
+      const int which = idx / (C * VPR);
+      const int rem = idx % (C * VPR);
+      const int r = rem / VPR, cv = rem % VPR;
+      if (idx < KQ_V) *reinterpret_cast<u32x4*>(which ? &sm.q[b][r][cv * EPV] : &sm.k[b][r][cv * EPV]) = pkq[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NM; j++) {
+      const int idx = tid + NTH * j;
+      if (idx < M_V) {
+        const int which = idx / (C * C / EPV);
+        const int rem = idx % (C * C / EPV);
+        const int r = rem / (C / EPV), cv = rem % (C / EPV);
+        *reinterpret_cast<u32x4*>(which ? &sm.p[b][r][cv * EPV] : &sm.tt[b][r][cv * EPV]) = pm[j];
       }
     }
-    __syncthreads();
-    // ---- P (state independent) and X = K S, Y = Q S
-    {
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
-      for (int t = wave; t < NRT * (NRT + 1) / 2; t += 4) {
-        int i = 0, rem = t;  // t -> (i, j), j <= i
-        while (rem > i) { rem -= i + 1; i++; }
-        const int j = rem;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mma<E, DK>(acc, &sm.q[16 * i][0], SM::KLD, &sm.k[16 * j][0], SM::KLD, lane);
-        const int s = 16 * j + c;
+    if (tid < V_V) {
+      const int r = tid / V_VPR, cv = tid % V_VPR;
+      const T* e = reinterpret_cast<const T*>(&pv);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int r = 16 * i + r0 + e;
-          const float v = s <= r ? __expf(sm.gam[r] - sm.gam[s]) * sm.rq[r] * sm.rk[s] * acc[e] : 0.f;
-          sm.p[r][s] = E::from_f32(v);
-        }
-      }
+      for (int i = 0; i < EPV; i++) sm.vt[b][cv * EPV + i][r] = E::to_f32(e[i]);
     }
-    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NRT) {
-      const int i = wave;
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
+    if (tid < S_V) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + tid * 4) = ps;
+  };
+
+  if (nchunks > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  T* obase = reinterpret_cast<T*>(a.o) + (long)h * a.dv + dv0 + 16 * tw + r4;
+  for (int ch = 0; ch < nchunks; ch++) {
+    const int b = DB ? (ch & 1) : 0;
+    const int nb = DB ? (b ^ 1) : 0;
+    const int sb = ch & 1;                 // state operand buffer read this chunk
+    const int cs = s0 + ch * C;
+    const int clen = min(C, s1 - cs);
+    __syncthreads();                       // B0: staged chunk and S^T visible
+    if (ch + 1 < nchunks) load_chunk(ch + 1);
+
+    // ---- X = K S, R = V - diag(a) X -> R^T
+    if (lw < NRT) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      X = tile_mma<E, DK>(X, &sm.k[16 * i][0], SM::KLD, &sm.st[0][0], SM::KLD, lane);
-      Y = tile_mma<E, DK>(Y, &sm.q[16 * i][0], SM::KLD, &sm.st[0][0], SM::KLD, lane);
-      f32x4 R;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 16 * i + r0 + e;
-        R[e] = sm.v[r][c] - sm.eg[r] * sm.rk[r] * X[e];
-      }
-      st_col4(&sm.rt[c][16 * i + r0], R);
+      X = tile_mma<E, DK>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
+      const int s = 16 * lw + r4;
+      st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
-    __syncthreads();
-    // ---- U = Tt R (Tt lower triangular: k < 16(i+1))
-    f32x4 U = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NRT) {
-      const int i = wave;
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
-      const int kend = ((16 * (i + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
-      U = tile_mma_rt<E>(U, &sm.tt[16 * i][0], SM::CLD, &sm.rt[0][0], SM::CLD, lane, kend);
-      f32x4 U2;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 16 * i + r0 + e;
-        U2[e] = sm.egc[r] * sm.rk[r] * U[e];
-      }
-      st_col4(&sm.ut[c][16 * i + r0], U);
-      st_col4(&sm.u2t[c][16 * i + r0], U2);
+    __syncthreads();                       // B1
+    // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
+    if (lw < NRT) {
+      const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
+      f32x4 U = {0.f, 0.f, 0.f, 0.f};
+      U = tile_mma_rt<E>(U, &sm.tt[b][16 * lw][0], CLD, &sm.rt[tw][0][0], CLD, lane, kend);
+      const int s = 16 * lw + r4;
+      st4(&sm.ut[tw][c16][s], U);
+      st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
-    __syncthreads();
-    // ---- O = diag(e^gamma rq) Y + P U
-    if (wave < NRT) {
-      const int i = wave;
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
-      const int kend = ((16 * (i + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
+    __syncthreads();                       // B2
+    // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
+    if (lw < NRT) {
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      Y = tile_mma<E, DK>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
+      const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 PU = {0.f, 0.f, 0.f, 0.f};
-      PU = tile_mma_rt<E>(PU, &sm.p[16 * i][0], SM::CLD, &sm.ut[0][0], SM::CLD, lane, kend);
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 16 * i + r0 + e;
-        if (r < clen) {
-          const float ov = sm.eg[r] * sm.rq[r] * Y[e] + PU[e];
-          op[((long)(cs + r) * a.hv + h) * a.dv + dv0 + c] = E::from_f32(ov);
-        }
-      }
+      PU = tile_mma_rt<E>(PU, &sm.ut[tw][0][0], CLD, &sm.p[b][16 * lw][0], CLD, lane, kend);
+      const int r = 16 * lw + c16;
+      if (r < clen) st4(obase + (long)(cs + r) * a.hv * a.dv, sm.sc[b][1][r] * Y + PU);
     }
-    // ---- S <- e^{gamma_last} S + K^T U2
+    // ---- S <- e^{gamma_last} S + K^T diag(c) U  -> S^T operand for the next chunk
     {
-      const int c = lane & 15, r0 = (lane >> 4) * 4;
-      const float gl = sm.gl;
+      const float gl = sm.sc[b][3][0];
 #pragma unroll
       for (int t = 0; t < STW; t++) {
-        const int rb = (wave * STW + t) * 16;
+        const int rb = (lw * STW + t) * 16;
         f32x4 acc = S[t] * gl;
-        if constexpr (SM::KT) {
-          acc = tile_mma<E, C>(acc, &sm.kt[SM::KT ? rb : 0][0], SM::CLD, &sm.u2t[0][0], SM::CLD, lane);
+        if constexpr (std::is_same<E, BF16>::value) {
+          acc = tile_mma_kt_bf16<C, KLD, SM::CW>(acc, &sm.k[b][0][0], rb, &sm.u2t[tw][0][0], CLD, lane);
         } else {
-          acc = tile_mma_at_f32<C>(acc, reinterpret_cast<const float*>(&sm.k[0][rb]), SM::KLD,
-                                   reinterpret_cast<const float*>(&sm.u2t[0][0]), SM::CLD, lane);
+          acc = tile_mma_at_f32<C>(acc, reinterpret_cast<const float*>(&sm.k[b][0][rb]), KLD,
+                                   reinterpret_cast<const float*>(&sm.u2t[tw][0][0]), CLD, lane);
         }
         S[t] = acc;
+        st4(&sm.st[sb ^ 1][tw][c16][rb + r4], acc);
       }
-      // st was last read by X, Y (two barriers ago): safe to rewrite now
-#pragma unroll
-      for (int t = 0; t < STW; t++) {
-        const int rb = (wave * STW + t) * 16;
-        st_col4(&sm.st[c][rb + r0], S[t]);
-      }
+    }
+    // ---- stage the next chunk (single-buffered: wait until all waves are
+    // done with this chunk's staged data)
+    if (ch + 1 < nchunks) {
+      if (!DB) __syncthreads();
+      store_chunk(nb);
     }
   }
 
   // ---- final state
   if (a.state_out) {
-    const int c = lane & 15, r0 = (lane >> 4) * 4;
     float* so = a.state_out + ((long)seq * a.hv + h) * DK * a.dv;
+    const int col = dv0 + 16 * tw + c16;
 #pragma unroll
     for (int t = 0; t < STW; t++) {
-      const int rb = (wave * STW + t) * 16;
+      const int rb = (lw * STW + t) * 16;
 #pragma unroll
-      for (int e = 0; e < 4; e++) so[(long)(rb + r0 + e) * a.dv + dv0 + c] = S[t][e];
+      for (int e = 0; e < 4; e++) so[(long)(rb + r4 + e) * a.dv + col] = S[t][e];
     }
   }
 }
@@ -602,16 +668,17 @@ hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
 
 template <class E, int C, int DK>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
-  const int GS = (a.hv / a.hk) * (a.dv / 16);
+  // bf16: two 16-column tiles per workgroup (8 waves), LDS double-buffered;
+  // fp32: one tile (4 waves), single-buffered (the fp32 tiles fill the LDS)
+  constexpr bool BF = std::is_same<E, BF16>::value;
+  constexpr int NT = BF ? 2 : 1;
+  const int GS = (a.hv / a.hk) * (a.dv / (16 * NT));
   const int ngroups = a.num_seqs * a.hk;
   const int per_xcd = (ngroups + 7) / 8;
-  dim3 grid(8 * per_xcd * GS), block(256);
-  hipLaunchKernelGGL((k_scan<E, C, DK>), grid, block, 0, s, a);
+  dim3 grid(8 * per_xcd * GS), block(256 * NT);
+  hipLaunchKernelGGL((k_scan<E, C, DK, NT, BF>), grid, block, 0, s, a);
   return hipGetLastError();
 }
-
-template <class E, template <class, int, int> class F>
-struct Dispatch;
 
 template <class E>
 hipError_t dispatch_prepare(const ScanArgs& a, hipStream_t s) {

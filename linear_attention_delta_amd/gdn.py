@@ -62,7 +62,7 @@ def _load():
         "gdn_conv1d": ([i32, i32, i32, P, i32, i32, i32, P, i64, P, P, P, i32, P, i64, P], i32),
         "gdn_prefill_workspace_size": ([D], sz),
         "gdn_prefill_chunked": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
-        "gdn_prefill_prepare": ([D, P, P, P, P, P, sz, P], i32),
+        "gdn_prefill_prepare": ([D, P, P, P, P, P, P, sz, P], i32),
         "gdn_prefill_scan": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
     }
@@ -185,8 +185,8 @@ class Prefill:
         self.ws = workspace if workspace is not None else alloc_workspace(self.dims, q.device)
         self.ws_bytes = self.ws.numel() * self.ws.element_size()
 
-    def prepare(self, k, g, beta, stream=None):
-        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(k), _ptr(g), _ptr(beta),
+    def prepare(self, q, k, g, beta, stream=None):
+        _check(lib.gdn_prefill_prepare(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(g), _ptr(beta),
                                        _ptr(self.cu_seqlens), _ptr(self.ws), self.ws_bytes, _stream(stream)))
 
     def scan(self, q, k, v, g, beta, o, state_in=None, state_out=None, stream=None):

@@ -92,12 +92,17 @@ def test_flags_scale_reserved(g):
 
 
 def test_workspace_size(g):
-    d = _dims(g)                       # dense: 64 chunks x 32 heads x 64 x 64 bf16
-    assert g.workspace_size(d) == 64 * 32 * 64 * 64 * 2
+    def a256(n):
+        return (n + 255) // 256 * 256
+    # dense: 64 chunks x 32 heads x (Tt, P: 2 x 64 x 64 bf16) + 4 x 64 fp32 scalars
+    d = _dims(g)
+    assert g.workspace_size(d) == a256(64 * 32 * 2 * 64 * 64 * 2) + a256(64 * 32 * 4 * 64 * 4)
     d = _dims(g, dtype=g.GDN_F32, chunk_size=32, seqlen=100, num_seqs=3, total_tokens=300)
-    assert g.workspace_size(d) == 3 * 4 * 32 * 32 * 32 * 4
+    units = 3 * 4 * 32
+    assert g.workspace_size(d) == a256(units * 2 * 32 * 32 * 4) + a256(units * 4 * 32 * 4)
     d = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5)   # varlen: table + upper bound of chunks
-    assert g.workspace_size(d) == 256 + (1000 // 64 + 5) * 32 * 64 * 64 * 2
+    units = (1000 // 64 + 5) * 32
+    assert g.workspace_size(d) == 256 + a256(units * 2 * 64 * 64 * 2) + a256(units * 4 * 64 * 4)
     assert g.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(g, chunk_size=8))) == 0
 
 
