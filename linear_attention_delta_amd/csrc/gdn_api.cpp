@@ -83,6 +83,8 @@ gdn_status check_dims(const gdn_dims* d, int op) {
                 (long long)sq, (long long)sk, (long long)qk_row, (long long)sv, (long long)v_row);
   if (sq % vec || sk % vec || sv % vec)
     return fail(GDN_ERR_INVALID_ARG, "token strides must be multiples of %lld elements", (long long)vec);
+  if (sq > (1 << 24) || sk > (1 << 24) || sv > (1 << 24))
+    return fail(GDN_ERR_UNSUPPORTED, "token strides above 2^24 elements are not supported");
   if (op == 0) {
     if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
       return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64 (got %d)", d->chunk_size);

@@ -659,6 +659,362 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   }
 }
 
+// ------------------------------------------------- phase 2, bf16 fast path
+//
+// One workgroup per (sequence, v-head, 16 columns of d_v), four waves with
+// fixed roles:
+//   wave 0  the state chain  X = K S -> R -> U = Tt R -> S <- gl S + K^T (c U)
+//   wave 1  the output       O^T = b (S^T Q^T) + U^T P^T
+//   waves 2, 3  stage the next chunk (K, K^T, Q, Tt, P, V^T, scalars) into
+//           the other half of a double-buffered LDS
+// Wave 0 keeps its d_k x 16 fp32 state slice in MFMA accumulator form for the
+// whole sequence.  An accumulator tile (lane (c, g) holds rows 4g..4g+3 of
+// column c) is fed straight back as the next product's operand by letting
+// the K index of one 16x16x32 step run over rows {32m + 4g + e} of two
+// stacked tiles: the other operand then reads the matching 2 x 4 elements
+// (two 8-byte LDS reads).  So no product of the chain goes through LDS; wave
+// 1 receives S and U through a small per-lane handoff in LDS.
+//
+// Per chunk: B0 | w0: X, R, U, handoff U | w1: S^T Q^T | w2,3: issue loads of
+// the next chunk | B1 | w0: S update, handoff S | w1: + U^T P^T, store O |
+// w2,3: write the next chunk to LDS.
+
+template <int C, int DK>
+struct alignas(16) ScanSmemBF {
+  static constexpr int KLD = DK + 8;   // 8-byte reads of 16 rows hit distinct banks
+  static constexpr int CLD = C + 8;
+  static constexpr int NRT = C / 16;
+  static constexpr int NDT = DK / 16;  // state row tiles
+  uint16_t k[2][C][KLD];
+  uint16_t kt[2][DK][CLD];
+  uint16_t q[2][C][KLD];
+  uint16_t tt[2][C][CLD];
+  uint16_t p[2][C][CLD];
+  uint16_t vt[2][16][CLD];
+  float sc[2][4][C];                   // a, b, c, e^{gamma_last}
+  uint32_t hs[2][64][NDT * 2 + 4];     // S handoff: per lane NDT tiles x 4 bf16
+  uint32_t hu[64][NRT * 2 + 4];        // U handoff: per lane NRT tiles x 4 bf16
+};
+
+__device__ __forceinline__ u32x2 pack4_bf16(f32x4 v) { return u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])}; }
+
+__device__ __forceinline__ bf16x8 frag2(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Two 8-byte pieces p[0..3], p[16..19] of a bf16 row: the operand half
+// matching rows {4g..4g+3} and {16+4g..16+4g+3} of two stacked tiles.
+__device__ __forceinline__ bf16x8 ld_frag2(const uint16_t* p) {
+  return frag2(*reinterpret_cast<const u32x2*>(p), *reinterpret_cast<const u32x2*>(p + 16));
+}
+
+__device__ __forceinline__ f32x4 ld4bf(const uint16_t* p) {
+  u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+// 4x4 bf16 block held as 4 rows of 8 bytes -> its transpose (4 rows of 8 bytes).
+__device__ __forceinline__ void transpose4x4(const u32x2 r[4], u32x2 t[4]) {
+  t[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
+  t[1] = u32x2{(r[0][0] >> 16) | (r[1][0] & 0xffff0000u), (r[2][0] >> 16) | (r[3][0] & 0xffff0000u)};
+  t[2] = u32x2{(r[0][1] & 0xffffu) | (r[1][1] << 16), (r[2][1] & 0xffffu) | (r[3][1] << 16)};
+  t[3] = u32x2{(r[0][1] >> 16) | (r[1][1] & 0xffff0000u), (r[2][1] >> 16) | (r[3][1] & 0xffff0000u)};
+}
+
+template <int C, int DK>
+__global__ void __launch_bounds__(256) k_scan_bf16(ScanArgs a) {
+  typedef ScanSmemBF<C, DK> SM;
+  constexpr int KLD = SM::KLD, CLD = SM::CLD, NRT = SM::NRT, NDT = SM::NDT;
+  constexpr int KS = DK / 32;          // 32-wide k steps over d_k
+  constexpr int PS = C / 32;           // 32-wide k steps over the chunk's tokens
+  static_assert(C % 32 == 0 && DK % 32 == 0, "chunk and d_k must be multiples of 32");
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4, r4 = 4 * g;
+
+  // ---- (sequence, v-head, 16-column tile), XCD-aware as in k_scan
+  const int nblk = a.dv / 16;
+  const int G = a.hv / a.hk;
+  const int GS = G * nblk;
+  const int ngroups = a.num_seqs * a.hk;
+  const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
+  const int grp = (m8 / GS) * 8 + xcd;
+  if (grp >= ngroups) return;
+  const int local = m8 % GS;
+  const int seq = grp / a.hk, hk = grp % a.hk;
+  const int vh = local / nblk;
+  const int h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
+  const int dv0 = (local % nblk) * 16;
+  int s0, s1, cbase;
+  if (a.seqlen > 0) {
+    s0 = seq * a.seqlen;
+    s1 = s0 + a.seqlen;
+    cbase = seq * ((a.seqlen + C - 1) / C);
+  } else {
+    s0 = a.cu_seqlens[seq];
+    s1 = a.cu_seqlens[seq + 1];
+    cbase = a.chunk_offsets[seq];
+  }
+  const int nchunks = (s1 - s0 + C - 1) / C;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
+  const uint16_t* mp = reinterpret_cast<const uint16_t*>(a.tinv);
+
+  // ---- staging (waves 2, 3): registers hold one chunk in flight
+  const int st = tid - 128;                  // staging thread 0..127
+  constexpr int KB = C * DK / 16;            // 4x4 blocks of K
+  constexpr int NKB = KB / 128;
+  constexpr int QV = C * DK / 8;             // 16-byte vectors of Q
+  constexpr int NQV = QV / 128;
+  constexpr int MV = 2 * C * C / 8;          // Tt and P vectors
+  constexpr int NMV = MV / 128;
+  constexpr int VB = C * 16 / 16;            // 4x4 blocks of the V slice
+  static_assert(NKB * 128 == KB && NQV * 128 == QV && NMV * 128 == MV && VB <= 128 && C <= 128, "staging");
+  u32x2 rk[NKB][4], rv[4];
+  u32x4 rq[NQV], rm[NMV], rs;
+  // Per-lane byte offsets inside a chunk, computed once; per chunk only the
+  // wave-uniform base pointers move.
+  unsigned kgo[NKB], qgo[NQV], vgo = 0;
+  const unsigned krow = (unsigned)a.stride_k * 2u, qrow = (unsigned)a.stride_q * 2u, vrow = (unsigned)a.stride_v * 2u;
+#pragma unroll
+  for (int j = 0; j < NKB; j++) {
+    const int blk = st + 128 * j, br = blk % (C / 4), bc = blk / (C / 4);
+    kgo[j] = (unsigned)(4 * br) * krow + 8u * bc;
+  }
+#pragma unroll
+  for (int j = 0; j < NQV; j++) {
+    const int idx = st + 128 * j, r = idx / (DK / 8), cv = idx % (DK / 8);
+    qgo[j] = (unsigned)r * qrow + 16u * cv;
+  }
+  if (st < VB) vgo = (unsigned)(4 * (st / 4)) * vrow + 8u * (st % 4);
+  const char* kbase = reinterpret_cast<const char*>(kp + (long)s0 * a.stride_k + (long)hk * DK);
+  const char* qbase = reinterpret_cast<const char*>(qp + (long)s0 * a.stride_q + (long)hk * DK);
+  const char* vbase = reinterpret_cast<const char*>(vp + (long)s0 * a.stride_v + (long)h * a.dv + dv0);
+  const char* mbase = reinterpret_cast<const char*>(mp + ((long)cbase * a.hv + h) * (2 * C * C));
+  const char* sbase = reinterpret_cast<const char*>(a.scal + ((long)cbase * a.hv + h) * (4 * C));
+  const long mstep = (long)a.hv * (2 * C * C) * 2, sstep = (long)a.hv * (4 * C) * 4;
+
+  auto load_chunk = [&](int ch) {
+    const int clen = min(C, s1 - (s0 + ch * C));
+    const char* kc = kbase + (long)ch * C * krow;
+    const char* qc = qbase + (long)ch * C * qrow;
+    const char* vc = vbase + (long)ch * C * vrow;
+    const char* mc = mbase + ch * mstep;
+    const char* sc = sbase + ch * sstep;
+    if (clen == C) {
+#pragma unroll
+      for (int j = 0; j < NKB; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) rk[j][e] = *reinterpret_cast<const u32x2*>(kc + kgo[j] + e * krow);
+#pragma unroll
+      for (int j = 0; j < NQV; j++) rq[j] = *reinterpret_cast<const u32x4*>(qc + qgo[j]);
+      if (st < VB)
+#pragma unroll
+        for (int e = 0; e < 4; e++) rv[e] = *reinterpret_cast<const u32x2*>(vc + vgo + e * vrow);
+    } else {  // partial last chunk: rows past the end read as zero
+#pragma unroll
+      for (int j = 0; j < NKB; j++) {
+        const int br = (st + 128 * j) % (C / 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          rk[j][e] = 4 * br + e < clen ? *reinterpret_cast<const u32x2*>(kc + kgo[j] + e * krow) : u32x2{0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < NQV; j++) {
+        const int r = (st + 128 * j) / (DK / 8);
+        rq[j] = r < clen ? *reinterpret_cast<const u32x4*>(qc + qgo[j]) : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (st < VB)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          rv[e] = 4 * (st / 4) + e < clen ? *reinterpret_cast<const u32x2*>(vc + vgo + e * vrow) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < NMV; j++) rm[j] = *reinterpret_cast<const u32x4*>(mc + 16 * (st + 128 * j));
+    if (st < C) rs = *reinterpret_cast<const u32x4*>(sc + 16 * st);
+  };
+  auto store_chunk = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < NKB; j++) {
+      const int blk = st + 128 * j, br = blk % (C / 4), bc = blk / (C / 4);
+      u32x2 t[4];
+      transpose4x4(rk[j], t);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        *reinterpret_cast<u32x2*>(&sm.k[b][4 * br + e][4 * bc]) = rk[j][e];
+        *reinterpret_cast<u32x2*>(&sm.kt[b][4 * bc + e][4 * br]) = t[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NQV; j++) {
+      const int idx = st + 128 * j, r = idx / (DK / 8), cv = idx % (DK / 8);
+      *reinterpret_cast<u32x4*>(&sm.q[b][r][8 * cv]) = rq[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NMV; j++) {
+      const int idx = st + 128 * j, which = idx / (C * C / 8), rem = idx % (C * C / 8);
+      const int r = rem / (C / 8), cv = rem % (C / 8);
+      *reinterpret_cast<u32x4*>(which ? &sm.p[b][r][8 * cv] : &sm.tt[b][r][8 * cv]) = rm[j];
+    }
+    if (st < VB) {
+      const int br = st / 4, bc = st % 4;
+      u32x2 t[4];
+      transpose4x4(rv, t);
+#pragma unroll
+      for (int e = 0; e < 4; e++) *reinterpret_cast<u32x2*>(&sm.vt[b][4 * bc + e][4 * br]) = t[e];
+    }
+    if (st < C) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + 4 * st) = rs;
+  };
+
+  // ---- wave 0: state slice in accumulator form; lane (c16, g) holds
+  // S[16u + 4g + e][dv0 + c16]
+  f32x4 S[NDT];
+  if (wave == 0) {
+    const float* sin = a.state_in ? a.state_in + ((long)seq * a.hv + h) * DK * a.dv : nullptr;
+#pragma unroll
+    for (int u = 0; u < NDT; u++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) S[u][e] = sin ? sin[(long)(16 * u + r4 + e) * a.dv + dv0 + c16] : 0.f;
+      *reinterpret_cast<u32x2*>(&sm.hs[0][lane][2 * u]) = pack4_bf16(S[u]);
+    }
+  }
+  if (wave >= 2 && nchunks > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)s0 * a.hv * a.dv + (long)h * a.dv + dv0 + r4;
+  const unsigned orow = (unsigned)(a.hv * a.dv);  // elements between tokens of o
+
+  // Each role runs its own loop with the same two barriers per chunk (the
+  // roles are wave-uniform, so every wave reaches every barrier), which keeps
+  // the roles' registers apart.
+  if (wave == 0) {
+    for (int ch = 0; ch < nchunks; ch++) {
+      const int b = ch & 1;
+      __syncthreads();  // B0: chunk ch staged
+      // X = K S: token tiles t, k steps m over d_k (rows 32m + {4g+e, 16+4g+e});
+      // all operand reads of the phase are issued before the first product
+      bf16x8 ak[KS][NRT];
+#pragma unroll
+      for (int m = 0; m < KS; m++)
+#pragma unroll
+        for (int t = 0; t < NRT; t++) ak[m][t] = ld_frag2(&sm.k[b][16 * t + c16][32 * m + r4]);
+      bf16x8 at[PS][NRT];
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++)
+#pragma unroll
+        for (int rt = 2 * pp; rt < NRT; rt++) at[pp][rt] = ld_frag2(&sm.tt[b][16 * rt + c16][32 * pp + r4]);
+      f32x4 X[NRT];
+#pragma unroll
+      for (int t = 0; t < NRT; t++) X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; m++) {
+        const bf16x8 bs = frag2(pack4_bf16(S[2 * m]), pack4_bf16(S[2 * m + 1]));
+#pragma unroll
+        for (int t = 0; t < NRT; t++) X[t] = mfma16(ak[m][t], bs, X[t]);
+      }
+      // R = V - diag(a) X, in the same layout (lane: 4 tokens of column c16)
+      f32x4 R[NRT];
+#pragma unroll
+      for (int t = 0; t < NRT; t++)
+        R[t] = ld4bf(&sm.vt[b][c16][16 * t + r4]) - ld4(&sm.sc[b][0][16 * t + r4]) * X[t];
+      // U = Tt R: row tiles rt, k steps p over token tile pairs (2p, 2p+1)
+      f32x4 U[NRT];
+#pragma unroll
+      for (int t = 0; t < NRT; t++) U[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++) {
+        const bf16x8 br = frag2(pack4_bf16(R[2 * pp]), pack4_bf16(R[2 * pp + 1]));
+#pragma unroll
+        for (int rt = 2 * pp; rt < NRT; rt++) U[rt] = mfma16(at[pp][rt], br, U[rt]);
+      }
+#pragma unroll
+      for (int t = 0; t < NRT; t++) {
+        *reinterpret_cast<u32x2*>(&sm.hu[lane][2 * t]) = pack4_bf16(U[t]);
+        U[t] = ld4(&sm.sc[b][2][16 * t + r4]) * U[t];  // U2 = diag(c) U
+      }
+      bf16x8 akt[PS][NDT];
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++)
+#pragma unroll
+        for (int u = 0; u < NDT; u++) akt[pp][u] = ld_frag2(&sm.kt[b][16 * u + c16][32 * pp + r4]);
+      const float gl = sm.sc[b][3][0];
+      __syncthreads();  // B1: U handoff written
+      // S <- e^{gamma_last} S + K^T U2: state tiles u, k steps p over token pairs
+#pragma unroll
+      for (int u = 0; u < NDT; u++) S[u] = S[u] * gl;
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++) {
+        const bf16x8 bu = frag2(pack4_bf16(U[2 * pp]), pack4_bf16(U[2 * pp + 1]));
+#pragma unroll
+        for (int u = 0; u < NDT; u++) S[u] = mfma16(akt[pp][u], bu, S[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NDT; u++) *reinterpret_cast<u32x2*>(&sm.hs[b ^ 1][lane][2 * u]) = pack4_bf16(S[u]);
+    }
+  } else if (wave == 1) {
+    for (int ch = 0; ch < nchunks; ch++) {
+      const int b = ch & 1;
+      const int cs = s0 + ch * C;
+      const int clen = min(C, s1 - cs);
+      __syncthreads();  // B0: chunk ch staged, S handoff for ch written
+      // Y^T = S^T Q^T: lane (c16, g) -> Y^T[4g + e][16t + c16]
+      bf16x8 aq[KS][NRT];
+#pragma unroll
+      for (int m = 0; m < KS; m++)
+#pragma unroll
+        for (int t = 0; t < NRT; t++) aq[m][t] = ld_frag2(&sm.q[b][16 * t + c16][32 * m + r4]);
+      bf16x8 ap[PS][NRT];
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++)
+#pragma unroll
+        for (int t = 2 * pp; t < NRT; t++) ap[pp][t] = ld_frag2(&sm.p[b][16 * t + c16][32 * pp + r4]);
+      f32x4 Y[NRT];
+#pragma unroll
+      for (int t = 0; t < NRT; t++) Y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; m++) {
+        const bf16x8 as = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.hs[b][lane][4 * m]));
+#pragma unroll
+        for (int t = 0; t < NRT; t++) Y[t] = mfma16(as, aq[m][t], Y[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NRT; t++) Y[t] = sm.sc[b][1][16 * t + c16] * Y[t];
+      __syncthreads();  // B1: U handoff written
+      // + U^T P^T, then store O
+#pragma unroll
+      for (int pp = 0; pp < PS; pp++) {
+        const bf16x8 au = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.hu[lane][4 * pp]));
+#pragma unroll
+        for (int t = 2 * pp; t < NRT; t++) Y[t] = mfma16(au, ap[pp][t], Y[t]);
+      }
+      uint16_t* oc = obase + (long)ch * C * orow;
+#pragma unroll
+      for (int t = 0; t < NRT; t++) {
+        const int r = 16 * t + c16;
+        if (r < clen) *reinterpret_cast<u32x2*>(oc + (unsigned)r * orow) = pack4_bf16(Y[t]);
+      }
+    }
+  } else {
+    for (int ch = 0; ch < nchunks; ch++) {
+      __syncthreads();  // B0
+      if (ch + 1 < nchunks) load_chunk(ch + 1);
+      __syncthreads();  // B1: this chunk's K^T and P reads are done only at B0 of the next
+      if (ch + 1 < nchunks) store_chunk((ch & 1) ^ 1);
+    }
+  }
+
+  if (wave == 0 && a.state_out) {
+    float* so = a.state_out + ((long)seq * a.hv + h) * DK * a.dv;
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) so[(long)(16 * u + r4 + e) * a.dv + dv0 + c16] = S[u][e];
+  }
+}
+
 template <class E, int C, int DK>
 hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
   dim3 grid(a.max_chunks, a.hv), block(256);
@@ -668,9 +1024,17 @@ hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
 
 template <class E, int C, int DK>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
-  // bf16: two 16-column tiles per workgroup (8 waves), LDS double-buffered;
-  // fp32: one tile (4 waves), single-buffered (the fp32 tiles fill the LDS)
   constexpr bool BF = std::is_same<E, BF16>::value;
+  if constexpr (BF && C % 32 == 0) {
+    // bf16 fast path: one 16-column tile per workgroup, role-split waves
+    const int GS = (a.hv / a.hk) * (a.dv / 16);
+    const int per_xcd = (a.num_seqs * a.hk + 7) / 8;
+    hipLaunchKernelGGL((k_scan_bf16<C, DK>), dim3(8 * per_xcd * GS), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  // general path: bf16 chunk 16 with two 16-column tiles per workgroup (8
+  // waves), LDS double-buffered; fp32 with one tile (4 waves), single-buffered
+  // (the fp32 tiles fill the LDS)
   constexpr int NT = BF ? 2 : 1;
   const int GS = (a.hv / a.hk) * (a.dv / (16 * NT));
   const int ngroups = a.num_seqs * a.hk;

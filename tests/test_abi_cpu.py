@@ -66,6 +66,7 @@ BAD = [
     (dict(chunk_size=48), 2), (dict(chunk_size=128), 2), (dict(dtype=7), 1),
     (dict(stride_q=100), 1), (dict(stride_v=4100), 1),  # too short / misaligned
     (dict(stride_k=2052), 1),
+    (dict(stride_q=(1 << 24) + 8), 2),
 ]
 
 
