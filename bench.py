@@ -60,19 +60,28 @@ def decode_alg_bytes(B, hk, hv, dk, dv, esize=2):
     return 2 * B * hv * dk * dv * 4 + B * (2 * hk * dk + 2 * hv * dv) * esize + 2 * B * hv * 4
 
 
-def source_digest():
+KERNEL_SOURCES = {"conv1d": "conv1d.hip", "prefill_prepare": "prefill.hip", "prefill_scan": "prefill.hip",
+                  "decode_step": "decode.hip"}
+
+
+def source_digest(kernel=None):
+    """Hash of the sources a kernel is built from: its own .hip file and the
+    shared device headers (all of csrc/ if kernel is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_delta_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if kernel is None else \
+        sorted([KERNEL_SOURCES[kernel], "gdn_device.h", "gdn_internal.h"])
+    for f in names:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
-    """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_counters.txt")
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kernel>.<workload>.counters.txt, if it was taken on the
+    kernel's current sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -80,7 +89,7 @@ def read_traffic(kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -106,6 +115,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=4, help="rotated buffer sets (MALL control)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 3 plain fp32 copies of 512 MiB (y = x * 1), so that a counter run can "
+                         "scale FETCH_SIZE / WRITE_SIZE by what they read for a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by "
@@ -118,6 +130,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- prefill
     inp = synth.prefill_4k_bf16()
@@ -142,10 +162,12 @@ def main():
         sets.append(dict(x=x, y=y, q=q, k=k, v=v, g=g, beta=beta, o=o, st=st, p=p))
     torch.cuda.synchronize()
 
+    conv_p = gdn.Conv1d(sets[0]["x"], w, seqlen=T)
+
     def step(s, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        gdn.conv1d(s["x"], w, seqlen=T, out=s["y"])
+        conv_p(s["x"], s["y"])
         if ev is not None:
             ev[1].record(stream)
         s["p"].prepare(s["q"], s["k"], s["g"], s["beta"])
@@ -198,7 +220,7 @@ def main():
     # the dominant kernel is charged with the bytes of the call it serves
     dom_bytes = {"conv1d": B_conv, "prefill_prepare": B_pre, "prefill_scan": B_pre}[dominant]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = read_traffic(dominant)
+    traffic = read_traffic(dominant, inp.name)
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "alg_bytes_per_launch": int(dom_bytes),
@@ -223,15 +245,18 @@ def main():
     kd = yd[:, ad:2 * ad].view(Bd, dsh.num_qk_heads, dsh.head_dim_k)
     vd = yd[:, 2 * ad:].view(Bd, dsh.num_v_heads, dsh.head_dim_v)
 
+    conv_d = gdn.Conv1d(xs[0], wd, seqlen=1, num_seqs=Bd)
+    dec = gdn.Decode(qd, kd, vd, num_slots=Bd)
+
     def dstep(i, ev=None):
         p = i % dinp.pool
         pool = i % npool
         if ev is not None:
             ev[0].record(stream)
-        gdn.conv1d(xs[p], wd, seqlen=1, num_seqs=Bd, conv_state=cwins[pool], out=yd)
+        conv_d(xs[p], yd, cwins[pool])
         if ev is not None:
             ev[1].record(stream)
-        gdn.decode_step(qd, kd, vd, gs[p], bs[p], pools[pool], out=od)
+        dec(qd, kd, vd, gs[p], bs[p], pools[pool], od)
         if ev is not None:
             ev[2].record(stream)
 
@@ -254,7 +279,7 @@ def main():
               "tokens_per_s": round(Bd / (dwall / args.decode_steps), 1),
               "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": read_traffic("decode_step"), "alg_bytes_per_launch": int(B_dec),
+                           "traffic": read_traffic("decode_step", dinp.name), "alg_bytes_per_launch": int(B_dec),
                            "avg_launch_us": round(d_step, 2)}}
 
     # ------------------------------------------------------------ CPU oracle
@@ -298,7 +323,7 @@ def main():
         "warm_single_set_us": {"conv1d": round(warm_conv, 2), "prefill_prepare": round(warm_prep, 2),
                                "prefill_scan": round(warm_scan, 2)},
         "decode": decode,
-        "source_digest": source_digest(),
+        "source_digest": {k: source_digest(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(out), flush=True)
 

@@ -145,6 +145,33 @@ def conv1d(x, weight, *, cu_seqlens=None, seqlen=None, num_seqs=None, bias=None,
     return out
 
 
+class Conv1d:
+    """Bound convolution call: sizes, weight and stream fixed at construction,
+    so that a loop of calls pays only the library call itself."""
+
+    def __init__(self, x, weight, *, cu_seqlens=None, seqlen=None, num_seqs=None, bias=None,
+                 activation=True, stride_y=None, stream=None):
+        n_tok, C = x.shape
+        if cu_seqlens is not None:
+            n_seq, sl = cu_seqlens.numel() - 1, 0
+        else:
+            sl = int(seqlen if seqlen is not None else n_tok)
+            n_seq = int(num_seqs if num_seqs is not None else (n_tok // sl if sl else 1))
+        self.shape = (n_tok, C)
+        self._fixed = (n_seq, n_tok, sl, _ptr(cu_seqlens), C, weight.shape[1], _dtype_code(x))
+        self._w = (_ptr(weight), _ptr(bias))
+        self._act = 1 if activation else 0
+        self._stride_x = x.stride(0)
+        self._stride_y = C if stride_y is None else stride_y
+        self._stream = _stream(stream)
+        self._keep = (weight, bias, cu_seqlens)
+
+    def __call__(self, x, y, conv_state=None):
+        _check(lib.gdn_conv1d(*self._fixed, x.data_ptr(), self._stride_x, *self._w, _ptr(conv_state),
+                              self._act, y.data_ptr(), self._stride_y, self._stream))
+        return y
+
+
 def _dims_for(q, k, v, *, num_seqs, seqlen, chunk_size, l2norm, heads_tiled, scale):
     n_tok, hk, dk = q.shape
     _, hv, dv = v.shape
@@ -214,6 +241,25 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, nu
         state_out = torch.empty((p.dims.num_seqs, hv, q.shape[2], dv), dtype=torch.float32, device=q.device)
     p(q, k, v, g, beta, out, state_in, state_out, stream)
     return out, state_out
+
+
+class Decode:
+    """Bound decode step: dims and stream fixed at construction (q, k, v of
+    the given shapes and token strides), reusable across steps and state
+    pools of num_slots slots."""
+
+    def __init__(self, q, k, v, *, num_slots, l2norm=True, heads_tiled=False, scale=1.0, stream=None):
+        self.dims = _dims_for(q, k, v, num_seqs=q.shape[0], seqlen=1, chunk_size=64, l2norm=l2norm,
+                              heads_tiled=heads_tiled, scale=scale)
+        self._d = ctypes.byref(self.dims)
+        self.num_slots = int(num_slots)
+        self._stream = _stream(stream)
+
+    def __call__(self, q, k, v, g, beta, state, out, state_slots=None):
+        _check(lib.gdn_decode_step(self._d, q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                   beta.data_ptr(), state.data_ptr(), self.num_slots, _ptr(state_slots),
+                                   out.data_ptr(), self._stream))
+        return out
 
 
 def decode_step(q, k, v, g, beta, state, *, state_slots=None, l2norm=True, heads_tiled=False, scale=1.0,
