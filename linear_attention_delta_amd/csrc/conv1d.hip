@@ -11,7 +11,7 @@
 //
 // Bit-exact arithmetic: acc = bias (or 0); acc = fma(w_j, x_j, acc) for
 // j = 0..W-1; y = acc / (1 + exp_cw(-acc)); bf16 output rounded to nearest
-// even.  Contraction is switched off in this file so the compiler adds or
+// even (NaN -> 0x7fc0).  Contraction is switched off in this file so the compiler adds or
 // removes no fused multiply-adds.
 #pragma clang fp contract(off)
 
@@ -26,29 +26,39 @@ struct Vec;  // 16 bytes of channels
 template <>
 struct Vec<BF16> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
-    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+  typedef u32x4 raw_t;
+  __device__ __forceinline__ static raw_t load_raw(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ static void cvt(raw_t w, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       out[2 * i] = __uint_as_float(w[i] << 16);
       out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ __forceinline__ static void load(const uint16_t* p, float* out) { cvt(load_raw(p), out); }
+  // Round to nearest even with the hardware conversion; a NaN is first made
+  // the canonical quiet NaN so that it converts to 0x7fc0 like f32_to_bf16.
   __device__ __forceinline__ static void store(uint16_t* p, const float* v) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; i++) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    for (int i = 0; i < 4; i++) {
+      const float lo = v[2 * i] != v[2 * i] ? __uint_as_float(0x7fc00000u) : v[2 * i];
+      const float hi = v[2 * i + 1] != v[2 * i + 1] ? __uint_as_float(0x7fc00000u) : v[2 * i + 1];
+      w[i] = cvt_bf16x2(lo, hi);
+    }
     *reinterpret_cast<u32x4*>(p) = w;
   }
 };
 template <>
 struct Vec<F32> {
   static constexpr int N = 4;
-  __device__ __forceinline__ static void load(const float* p, float* out) {
-    f32x4 w = *reinterpret_cast<const f32x4*>(p);
+  typedef f32x4 raw_t;
+  __device__ __forceinline__ static raw_t load_raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ static void cvt(raw_t w, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; i++) out[i] = w[i];
   }
+  __device__ __forceinline__ static void load(const float* p, float* out) { cvt(load_raw(p), out); }
   __device__ __forceinline__ static void store(float* p, const float* v) {
     f32x4 w = {v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(p) = w;
@@ -67,7 +77,7 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int t) {
   return lo;
 }
 
-template <class E, int W, int TOK>
+template <class E, int W, int TOK, bool ACT>
 __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
   typedef typename E::store_t T;
   constexpr int V = Vec<E>::N;
@@ -102,20 +112,26 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
   }
 
   // Fast path: the block and its W-1 token halo lie inside one sequence.
-  // Issue all TOK + W - 1 row loads at once, then compute.
+  // Issue all TOK + W - 1 row loads at once, then walk the tokens with the
+  // last W inputs converted to fp32 in a sliding register window.
   if (t_end - t_begin == TOK && t_begin - (W - 1) >= seq_start && t_end <= seq_end) {
-    float rows[TOK + W - 1][V];
+    typename Vec<E>::raw_t raw[TOK + W - 1];
 #pragma unroll
-    for (int j = 0; j < TOK + W - 1; j++) Vec<E>::load(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0, rows[j]);
+    for (int j = 0; j < TOK + W - 1; j++)
+      raw[j] = Vec<E>::load_raw(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0);
+    float win[W][V];
+#pragma unroll
+    for (int j = 0; j < W - 1; j++) Vec<E>::cvt(raw[j], win[j]);
 #pragma unroll
     for (int tt = 0; tt < TOK; tt++) {
+      Vec<E>::cvt(raw[tt + W - 1], win[(tt + W - 1) % W]);
       float out[V];
 #pragma unroll
       for (int i = 0; i < V; i++) {
         float acc = bias[i];
 #pragma unroll
-        for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], rows[tt + j][i], acc);
-        out[i] = a.activation ? silu_exact(acc) : acc;
+        for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], win[(tt + j) % W][i], acc);
+        out[i] = ACT ? silu_exact(acc) : acc;
       }
       Vec<E>::store(y + (long)(t_begin + tt) * a.stride_y + c0, out);
     }
@@ -162,7 +178,7 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
       float acc = bias[i];
 #pragma unroll
       for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], hist[j][i], acc);
-      out[i] = a.activation ? silu_exact(acc) : acc;
+      out[i] = ACT ? silu_exact(acc) : acc;
     }
     Vec<E>::store(y + (long)t * a.stride_y + c0, out);
 #pragma unroll
@@ -264,7 +280,10 @@ hipError_t launch_w(const ConvArgs& a, hipStream_t s) {
   }
   if (a.total_tokens > 0) {
     dim3 grid((a.total_tokens + kConvTok - 1) / kConvTok, (groups + 255) / 256);
-    hipLaunchKernelGGL((k_conv1d<E, W, kConvTok>), grid, block, 0, s, a);
+    if (a.activation)
+      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, false>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -138,14 +138,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // with C1 = ln2 cut to 16 significant bits (n C1 exact for |n| < 256) and
 // C2 = fp32(ln2 - C1); e^r by its Taylor series through r^7 in Horner form
 // with fused multiply-adds; then scaled by 2^n.  Inputs above 88.5 give
-// +inf, below -86 give 0, so every finite result is a normal number.  The
-// operation order is fixed so that the convolution's output is a function of
-// its inputs alone, reproducible bit for bit by any IEEE fp32 machine that
-// follows the same steps.
+// +inf, below -86 give 0, so every finite result is a normal number; NaN
+// gives itself.  The operation order is fixed so that the convolution's
+// output is a function of its inputs alone, reproducible bit for bit by any
+// IEEE fp32 machine that follows the same steps.  The three special ranges
+// are selected at the end rather than branched on, so a wave never splits.
 __device__ __forceinline__ float exp_cw(float x) {
-  if (x != x) return x;
-  if (x > 88.5f) return __builtin_inff();
-  if (x < -86.0f) return 0.0f;
   const float c1 = 0.693145751953125f;          // 45426 / 65536
   const float c2 = (float)(0.69314718055994530942 - 0.693145751953125);
   const float inv_ln2 = (float)(1.0 / 0.69314718055994530942);
@@ -160,7 +158,12 @@ __device__ __forceinline__ float exp_cw(float x) {
   p = __builtin_fmaf(p, r, 0.5f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  return __builtin_ldexpf(p, (int)n);
+  // in range |n| <= 128; the clamp only keeps the integer conversion defined
+  // for inputs whose result is replaced below
+  float e = __builtin_ldexpf(p, (int)__builtin_fminf(__builtin_fmaxf(n, -200.0f), 200.0f));
+  e = x > 88.5f ? __builtin_inff() : e;
+  e = x < -86.0f ? 0.0f : e;
+  return x != x ? x : e;
 }
 
 }  // namespace gdn

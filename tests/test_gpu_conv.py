@@ -114,3 +114,27 @@ def test_conv_qwen35_4k_bitexact(G, orc):
     got = _bits(y)
     bad = int(np.sum(got != ref))
     assert bad == 0, f"{bad} mismatching elements"
+
+
+def test_conv_special_values_bitexact(G, orc):
+    """Zeros, bf16 subnormals, the largest finite values, infinities and NaNs
+    (both signs, with payloads) through conv + SiLU: the output bits still
+    equal the oracle's fp32 definition (NaN results are the canonical 0x7fc0)."""
+    import torch
+    note("conv special values bf16")
+    r = np.random.default_rng(11)
+    T, C, W = 48, 64, 4
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007f, 0x807f, 0x0080, 0x8080, 0x7f7f, 0xff7f,
+                         0x7f80, 0xff80, 0x7fc0, 0xffc0, 0x7fa1, 0xffc1, 0x3f80, 0xbf80, 0x4200, 0xc2b1,
+                         0x42b2, 0xc2b2, 0x42ae, 0xc2ae], dtype=np.uint16)
+    normal = synth.bf16_bits(r.normal(size=(T, C)).astype(np.float32))
+    bits = np.where(r.random((T, C)) < 0.35, specials[r.integers(0, len(specials), (T, C))], normal).astype(np.uint16)
+    x = (bits.astype(np.uint32) << 16).view(np.float32)
+    w = np.array([1.0, -1.0, 0.5, 2.0, 1e-3, -3.0, 0.0, 1e20], dtype=np.float32)[r.integers(0, 8, (C, W))]
+    cu = np.array([0, 17, T], dtype=np.int32)
+    y = G.conv1d(bits_to_dev(bits), to_dev(w), cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    ref = orc.conv1d_f32(x, w, cu, out_bf16=True)
+    got = _bits(y)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]:#06x} want {ref[tuple(bad[0])]:#06x}"
