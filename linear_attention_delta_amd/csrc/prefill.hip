@@ -16,8 +16,9 @@
 //   O  = diag(b) Q S + P U
 //   S <- e^{gamma_last} S + K^T diag(c) U
 //
-// Phase 1 (k_prepare): one workgroup per (chunk, v-head), fully parallel.
-// It forms K K^T and K Q^T on the matrix cores, inverts I + A blockwise --
+// Phase 1 (k_prepare): one workgroup per (chunk, q/k head, pair of v-heads),
+// fully parallel.  It forms K K^T and K Q^T on the matrix cores, inverts
+// I + A blockwise --
 // the doubling product (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8) on each 16x16
 // diagonal block (N^16 = 0), then pairwise merging 16 -> 32 -> 64 with
 // [[X,0],[Y,Z]]^{-1} = [[X^-1,0],[-Z^-1 Y X^-1, Z^-1]] -- never powers of the
@@ -130,34 +131,90 @@ __device__ __forceinline__ void st16_plus_i(float* D, int ldd, f32x4 v, int lane
 }
 
 // ---------------------------------------------------------------- phase 1
-
+//
+// One workgroup per (chunk, q/k head, HPW of the v-heads that read it): K
+// and Q are staged once, the raw products K K^T and Q K^T are formed once
+// on the matrix cores and scaled per v-head (the decays and beta are per
+// v-head).  The chunk inverse runs in registers on 16x16 fp32 tiles held in
+// the accumulator layout (lane (c, g) holds T[4g+e][c]); a product X Y is
+// four 16x16x4 steps whose k index runs over {4g + t}, so its operands are
+// X^T and Y in that same layout and no lane exchange is needed.
 // Workspace block of one (chunk, v-head): Tt [C][C] then P [C][C] in the
 // operand type, and (separately) 4 x C fp32 scalars: a, b, c and
 // e^{gamma_last} (first element of the fourth row).
-template <class E, int C, int DK>
+
+template <class E, int C, int DK, int HPW>
 struct alignas(16) PrepSmem {
   typedef typename E::store_t T;
   static constexpr int KLD = DK + 16 / sizeof(T);  // row pad: 16 bytes
   static constexpr int ALD = C + 4;                // 16-byte aligned rows
-  static constexpr int SLD = 17;
-  T k[C][KLD];
-  T q[C][KLD];
-  float at[C][ALD];            // A, then (I + A)^{-1} in place
-  float sc[4][4][16][SLD];     // per-wave 16x16 scratch
-  float w1[32][33];
-  float gam[C], bet[C], rk[C], rq[C];
+  union U {
+    struct { T k[C][KLD]; T q[C][KLD]; } in;       // Gram operands
+    float at[HPW][C][ALD];                         // A per v-head, then its inverse in place
+  } u;
+  float gam[HPW][C], bet[HPW][C], rk[C], rq[C];
 };
 
-template <class E, int C, int DK>
+// X Y for 16x16 fp32 tiles given X^T and Y in the accumulator layout.
+__device__ __forceinline__ f32x4 mm_tt(f32x4 xt, f32x4 y) {
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; t++) d = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[t], y[t], d, 0, 0, 0);
+  return d;
+}
+
+// 16x16 tile of a row-major fp32 array (leading dimension L) in the
+// accumulator layout, as itself (ld_c) or transposed (ld_ct).
+__device__ __forceinline__ f32x4 ld_c(const float* M, int L, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  return f32x4{M[(4 * g) * L + c], M[(4 * g + 1) * L + c], M[(4 * g + 2) * L + c], M[(4 * g + 3) * L + c]};
+}
+__device__ __forceinline__ f32x4 ld_ct(const float* M, int L, int lane) {
+  return *reinterpret_cast<const f32x4*>(M + (lane & 15) * L + 4 * (lane >> 4));
+}
+__device__ __forceinline__ void st_c(float* M, int L, f32x4 v, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; e++) M[(4 * g + e) * L + c] = v[e];
+}
+__device__ __forceinline__ f32x4 ident_c(int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  return f32x4{4 * g == c ? 1.f : 0.f, 4 * g + 1 == c ? 1.f : 0.f, 4 * g + 2 == c ? 1.f : 0.f,
+               4 * g + 3 == c ? 1.f : 0.f};
+}
+
+// (I + N)^{-1} of a strictly lower 16x16 block N (row-major at A0) by the
+// doubling product (I - N)(I + N^2)(I + N^4)(I + N^8), N^16 = 0.  The
+// factors are polynomials in N and commute, so each step multiplies from the
+// side whose transpose is at hand.
+__device__ __forceinline__ f32x4 inv16(const float* A0, int L, int lane) {
+  const f32x4 id = ident_c(lane);
+  const f32x4 n = ld_c(A0, L, lane), nt = ld_ct(A0, L, lane);
+  const f32x4 n2 = mm_tt(nt, n), n2t = mm_tt(n, nt);
+  const f32x4 n4 = mm_tt(n2t, n2), n4t = mm_tt(n2, n2t);
+  const f32x4 n8t = mm_tt(n4, n4t);
+  const f32x4 x1 = mm_tt(id - nt, id + n2);   // (I - N)(I + N^2)
+  const f32x4 x2 = mm_tt(id + n4t, x1);       // (I + N^4) x1
+  return mm_tt(id + n8t, x2);                 // (I + N^8) x2
+}
+
+template <class E, int C, int DK, int HPW>
 __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   typedef typename E::store_t T;
-  typedef PrepSmem<E, C, DK> SM;
+  typedef PrepSmem<E, C, DK, HPW> SM;
   constexpr int NRT = C / 16;
+  constexpr int NT = NRT * (NRT + 1) / 2;      // lower 16x16 tiles (diagonal included)
+  constexpr int NTW = (NT + 3) / 4;            // per wave
+  constexpr int L = SM::ALD;
   __shared__ SM sm;
-  const int h = blockIdx.y;
   int seq, start, len;
   if (!chunk_of(a, C, blockIdx.x, seq, start, len)) return;
-  const int hk = a.tiled ? (h % a.hk) : (h / (a.hv / a.hk));
+  const int G = a.hv / a.hk;
+  const int hk = blockIdx.y / (G / HPW);
+  const int vh0 = (blockIdx.y % (G / HPW)) * HPW;
+  int hs[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; j++) hs[j] = a.tiled ? (hk + (vh0 + j) * a.hk) : (hk * G + vh0 + j);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
@@ -184,9 +241,9 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       }
     }
     float gv = 0.f, bv = 0.f;
-    if (wave == 0 && lane < len) {
-      gv = a.g[(long)(start + lane) * a.hv + h];
-      bv = a.beta[(long)(start + lane) * a.hv + h];
+    if (wave < HPW && lane < len) {
+      gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
+      bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
     }
 #pragma unroll
     for (int j = 0; j < NV; j++) {
@@ -194,7 +251,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       const int which = idx / (C * VPR);
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
-      *reinterpret_cast<u32x4*>(which ? &sm.q[r][cv * EPV] : &sm.k[r][cv * EPV]) = w[j];
+      *reinterpret_cast<u32x4*>(which ? &sm.u.in.q[r][cv * EPV] : &sm.u.in.k[r][cv * EPV]) = w[j];
       const T* e = reinterpret_cast<const T*>(&w[j]);
       float ss = 0.f;
 #pragma unroll
@@ -208,143 +265,168 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
         if (which) sm.rq[r] = a.scale * inv; else sm.rk[r] = inv;
       }
     }
-    if (wave == 0) {
+    if (wave < HPW) {
       const float gm = wave_prefix_sum(gv, lane);
       if (lane < C) {
-        sm.gam[lane] = gm;
-        sm.bet[lane] = bv;
+        sm.gam[wave][lane] = gm;
+        sm.bet[wave][lane] = bv;
       }
     }
   }
   __syncthreads();
-  // ---- transposed Gram tiles D[s][r] = k_s . x_r (x = k or q), s-block j,
-  // r-block i: each lane then owns 4 consecutive s of one row r.
-  //   A[r][s] = beta_r rk_r rk_s e^{gamma_r - gamma_s} k_r.k_s  (s < r)  -> LDS
-  //   P[r][s] = rq_r rk_s e^{gamma_r - gamma_s} q_r.k_s         (s <= r) -> workspace
-  {
-    T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + h) * (2 * C * C) + C * C;
-    for (int t = wave; t < 2 * NRT * NRT; t += 4) {
-      const int which = t / (NRT * NRT);  // 0: A, 1: P
-      const int i = (t % (NRT * NRT)) / NRT, j = t % NRT;
-      const int r = 16 * i + c16, s0 = 16 * j + r4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (j <= i) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mma<E, DK>(acc, &sm.k[16 * j][0], SM::KLD, which ? &sm.q[16 * i][0] : &sm.k[16 * i][0],
-                              SM::KLD, lane);
-        const float gr = sm.gam[r];
-        const float fr = which ? sm.rq[r] : sm.bet[r] * sm.rk[r];
+  // ---- transposed Gram tiles D[s][r] = k_s . x_r (x = k or q) of the lower
+  // tile (i, j), j <= i: lane (c, g) holds r = 16i + c, s = 16j + 4g + e.
+  //   P[r][s] = rq_r rk_s e^{gamma_r - gamma_s} q_r.k_s          (s <= r) -> workspace
+  //   A[r][s] = beta_r rk_r rk_s e^{gamma_r - gamma_s} k_r.k_s   (s < r)  -> registers, then LDS
+  auto tile_ij = [](int t, int& i, int& j) {
+    i = 0;
+    while ((i + 1) * (i + 2) / 2 <= t) i++;
+    j = t - i * (i + 1) / 2;
+  };
+  f32x4 rawA[NTW];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int s = s0 + e;
-          const bool keep = which ? (s <= r) : (s < r);
-          v[e] = keep ? fr * sm.rk[s] * __expf(gr - sm.gam[s]) * acc[e] : 0.f;
-        }
+  for (int n = 0; n < NTW; n++) {
+    const int t = wave + 4 * n;
+    if (t < NT) {
+      int i, j;
+      tile_ij(t, i, j);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      rawA[n] = tile_mma<E, DK>(acc, &sm.u.in.k[16 * j][0], SM::KLD, &sm.u.in.k[16 * i][0], SM::KLD, lane);
+    }
+  }
+  for (int t = wave; t < NT; t += 4) {
+    int i, j;
+    tile_ij(t, i, j);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile_mma<E, DK>(acc, &sm.u.in.k[16 * j][0], SM::KLD, &sm.u.in.q[16 * i][0], SM::KLD, lane);
+    const int r = 16 * i + c16, s0 = 16 * j + r4;
+    const float fr = sm.rq[r];
+#pragma unroll
+    for (int hh = 0; hh < HPW; hh++) {
+      const float gr = sm.gam[hh][r];
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int s = s0 + e;
+        v[e] = s <= r ? fr * sm.rk[s] * __expf(gr - sm.gam[hh][s]) * acc[e] : 0.f;
       }
-      if (which == 0) {
-        *reinterpret_cast<f32x4*>(&sm.at[r][s0]) = v;
-      } else if constexpr (std::is_same<E, BF16>::value) {
-        u32x2 w2 = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(pout + r * C + s0) = w2;
+      T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C) + C * C;
+      if constexpr (std::is_same<E, BF16>::value) {
+        *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
       } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(pout) + r * C + s0) = v;
       }
     }
   }
+  // upper tiles of P are zero (the scan reads P in whole 32-column steps)
+  for (int t = wave; t < NRT * NRT; t += 4) {
+    const int i = t / NRT, j = t % NRT;
+    if (j <= i) continue;
+    const int r = 16 * i + c16, s0 = 16 * j + r4;
+#pragma unroll
+    for (int hh = 0; hh < HPW; hh++) {
+      T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C) + C * C;
+      if constexpr (std::is_same<E, BF16>::value) {
+        *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{0u, 0u};
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(pout) + r * C + s0) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
   // ---- per-token scalars a, b, c and e^{gamma_last}
-  if (wave == 1 && lane < C) {
-    float* scal = a.scal + ((long)blockIdx.x * a.hv + h) * (4 * C);
-    const float gm = sm.gam[lane], glast = sm.gam[C - 1];
+  if (wave < HPW && lane < C) {
+    float* scal = a.scal + ((long)blockIdx.x * a.hv + hs[wave]) * (4 * C);
+    const float gm = sm.gam[wave][lane], glast = sm.gam[wave][C - 1];
     const float eg = __expf(gm);
     scal[lane] = eg * sm.rk[lane];
     scal[C + lane] = eg * sm.rq[lane];
     scal[2 * C + lane] = __expf(glast - gm) * sm.rk[lane];
     scal[3 * C + lane] = lane == 0 ? __expf(glast) : 0.f;
   }
-  __syncthreads();
-  // ---- 16x16 diagonal blocks: (I+N)^{-1} = (I-N)(I+N^2)(I+N^4)(I+N^8)
-  if (wave < C / 16) {
-    float* N = &sm.at[16 * wave][16 * wave];
-    float* s0 = &sm.sc[wave][0][0][0];
-    float* s1 = &sm.sc[wave][1][0][0];
-    float* s2 = &sm.sc[wave][2][0][0];
-    float* s3 = &sm.sc[wave][3][0][0];
-    constexpr int L = SM::ALD, S = SM::SLD;
-    f32x4 n2 = mm16_f32<16>(N, L, N, L, lane);
-    st16(s0, S, n2, lane);
-    wave_lds_sync();
-    f32x4 n4 = mm16_f32<16>(s0, S, s0, S, lane);
-    st16(s1, S, n4, lane);
-    wave_lds_sync();
-    f32x4 n8 = mm16_f32<16>(s1, S, s1, S, lane);
-    st16_plus_i(s2, S, n8, lane);  // I + N^8
-    st16_plus_i(s0, S, n2, lane);  // I + N^2
-    st16_plus_i(s1, S, n4, lane);  // I + N^4
-    {  // I - N
+  __syncthreads();  // K and Q are dead: A takes their place
 #pragma unroll
-      for (int e = 0; e < 4; e++) s3[(r4 + e) * S + c16] = (r4 + e == c16 ? 1.f : 0.f) - N[(r4 + e) * L + c16];
+  for (int n = 0; n < NTW; n++) {
+    const int t = wave + 4 * n;
+    if (t < NT) {
+      int i, j;
+      tile_ij(t, i, j);
+      const int r = 16 * i + c16, s0 = 16 * j + r4;
+      const float fr = sm.rk[r];
+#pragma unroll
+      for (int hh = 0; hh < HPW; hh++) {
+        const float gr = sm.gam[hh][r], br = sm.bet[hh][r] * fr;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int s = s0 + e;
+          v[e] = s < r ? br * sm.rk[s] * __expf(gr - sm.gam[hh][s]) * rawA[n][e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(&sm.u.at[hh][r][s0]) = v;
+      }
     }
-    wave_lds_sync();
-    f32x4 p = mm16_f32<16>(s3, S, s0, S, lane);
-    wave_lds_sync();
-    st16(s3, S, p, lane);
-    wave_lds_sync();
-    p = mm16_f32<16>(s3, S, s1, S, lane);
-    wave_lds_sync();
-    st16(s3, S, p, lane);
-    wave_lds_sync();
-    p = mm16_f32<16>(s3, S, s2, S, lane);
-    st16(N, L, p, lane);
   }
   __syncthreads();
-  // ---- merge 16 -> 32: lower-left block L = -Z (Y X)
-  if (C >= 32 && wave < C / 32) {
-    const int b = 32 * wave;
-    constexpr int L = SM::ALD, S = SM::SLD;
-    float* X = &sm.at[b][b];
-    float* Z = &sm.at[b + 16][b + 16];
-    float* Y = &sm.at[b + 16][b];
-    float* s0 = &sm.sc[wave][0][0][0];
-    f32x4 w = mm16_f32<16>(Y, L, X, L, lane);
-    st16(s0, S, w, lane);
-    wave_lds_sync();
-    f32x4 l = mm16_f32<16>(Z, L, s0, S, lane);
-    st16(Y, L, -l, lane);
+  // ---- diagonal 16x16 blocks, inverted in registers, written back in place
+  for (int blk = wave; blk < HPW * NRT; blk += 4) {
+    const int hh = blk / NRT, d = blk % NRT;
+    float* A0 = &sm.u.at[hh][16 * d][16 * d];
+    const f32x4 inv = inv16(A0, L, lane);
+    st_c(A0, L, inv, lane);
   }
   __syncthreads();
-  // ---- merge 32 -> 64
-  if (C == 64) {
-    constexpr int L = SM::ALD;
-    const int i = wave >> 1, j = wave & 1;  // 16x16 tile of the 32x32 block
-    // W1 = Y X with Y = A[32:64, 0:32], X = inv[0:32, 0:32] (lower: k >= j)
-    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = j; kb < 2; kb++) {
-      f32x4 t = mm16_f32<16>(&sm.at[32 + 16 * i][16 * kb], L, &sm.at[16 * kb][16 * j], L, lane);
-      w += t;
+  // ---- merge 16 -> 32: [[X, 0], [Y, Z]]^{-1} has lower-left block -Z (Y X)
+  if constexpr (C >= 32) {
+    for (int m = wave; m < HPW * (NRT / 2); m += 4) {
+      const int hh = m / (NRT / 2), b = 32 * (m % (NRT / 2));
+      float* at = &sm.u.at[hh][0][0];
+      const f32x4 w = mm_tt(ld_ct(at + (b + 16) * L + b, L, lane), ld_c(at + b * L + b, L, lane));
+      const f32x4 l = mm_tt(ld_ct(at + (b + 16) * L + b + 16, L, lane), w);
+      st_c(at + (b + 16) * L + b, L, -l, lane);
     }
-    st16(&sm.w1[16 * i][16 * j], 33, w, lane);
     __syncthreads();
-    // L = -Z W1 with Z = inv[32:64, 32:64] (lower: k <= i)
-    f32x4 l = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb <= i; kb++) {
-      f32x4 t = mm16_f32<16>(&sm.at[32 + 16 * i][32 + 16 * kb], L, &sm.w1[16 * kb][16 * j], 33, lane);
-      l += t;
-    }
-    st16(&sm.at[32 + 16 * i][16 * j], L, -l, lane);
   }
-  __syncthreads();
+  // ---- merge 32 -> 64: lower-left 32x32 block -Z (Y X), one 16-column
+  // strip jc of it per wave; Y is still the original A there
+  if constexpr (C == 64) {
+    f32x4 l2 = {0.f, 0.f, 0.f, 0.f}, l3 = {0.f, 0.f, 0.f, 0.f};
+    const int hh = wave >> 1, jc = wave & 1;
+    const bool act = hh < HPW;
+    float* at = &sm.u.at[act ? hh : 0][0][0];
+    auto blk = [&](int bi, int bj) { return at + 16 * bi * L + 16 * bj; };
+    if (act) {
+      f32x4 w2, w3;
+      if (jc == 0) {  // W_i0 = A_i0 X00 + A_i1 X10
+        const f32x4 x00 = ld_c(blk(0, 0), L, lane), x10 = ld_c(blk(1, 0), L, lane);
+        w2 = mm_tt(ld_ct(blk(2, 0), L, lane), x00) + mm_tt(ld_ct(blk(2, 1), L, lane), x10);
+        w3 = mm_tt(ld_ct(blk(3, 0), L, lane), x00) + mm_tt(ld_ct(blk(3, 1), L, lane), x10);
+      } else {        // W_i1 = A_i1 X11
+        const f32x4 x11 = ld_c(blk(1, 1), L, lane);
+        w2 = mm_tt(ld_ct(blk(2, 1), L, lane), x11);
+        w3 = mm_tt(ld_ct(blk(3, 1), L, lane), x11);
+      }
+      // L_2j = -Z22 W_2j ; L_3j = -(Z32 W_2j + Z33 W_3j)
+      l2 = -mm_tt(ld_ct(blk(2, 2), L, lane), w2);
+      l3 = -(mm_tt(ld_ct(blk(3, 2), L, lane), w2) + mm_tt(ld_ct(blk(3, 3), L, lane), w3));
+    }
+    __syncthreads();  // every wave has read the original A blocks
+    if (act) {
+      st_c(blk(2, jc), L, l2, lane);
+      st_c(blk(3, jc), L, l3, lane);
+    }
+    __syncthreads();
+  }
   // ---- Tt = inv diag(beta), upper triangle zero, to the workspace
-  {
-    T* out = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + h) * (2 * C * C);
+#pragma unroll
+  for (int hh = 0; hh < HPW; hh++) {
+    T* out = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C);
     for (int idx = tid; idx < C * C / 4; idx += 256) {
       const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.at[r][s0]);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0]);
       f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * sm.bet[s0 + e] : 0.f;
+      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * sm.bet[hh][s0 + e] : 0.f;
       if constexpr (std::is_same<E, BF16>::value) {
-        u32x2 w2 = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(out + r * C + s0) = w2;
+        *reinterpret_cast<u32x2*>(out + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
       } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + r * C + s0) = v;
       }
@@ -1033,8 +1115,14 @@ __global__ void __launch_bounds__(512) k_scan_bf16(ScanArgs a) {
 
 template <class E, int C, int DK>
 hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
-  dim3 grid(a.max_chunks, a.hv), block(256);
-  hipLaunchKernelGGL((k_prepare<E, C, DK>), grid, block, 0, s, a);
+  const int G = a.hv / a.hk;
+  if (G % 2 == 0) {
+    dim3 grid(a.max_chunks, a.hv / 2), block(256);
+    hipLaunchKernelGGL((k_prepare<E, C, DK, 2>), grid, block, 0, s, a);
+  } else {
+    dim3 grid(a.max_chunks, a.hv), block(256);
+    hipLaunchKernelGGL((k_prepare<E, C, DK, 1>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -36,10 +36,16 @@ def _run_gpu(G, inp, y, *, chunk=None, state0=None, heads_tiled=False, scale=Non
     q, k, v = _dev_qkv(y, sh, inp.dtype)
     cu = None if inp.dense_T else torch.from_numpy(inp.cu_seqlens).cuda()
     s0 = None if state0 is None else torch.from_numpy(np.ascontiguousarray(state0, dtype=np.float32)).cuda()
-    o, S = G.prefill(q, k, v, to_dev(inp.g), to_dev(inp.beta), state_in=s0, cu_seqlens=cu,
-                     seqlen=inp.dense_T if inp.dense_T else None, num_seqs=inp.num_seqs,
-                     chunk_size=chunk or inp.chunk_size, heads_tiled=heads_tiled,
-                     scale=inp.scale if scale is None else scale, l2norm=l2norm)
+    # workspace and outputs start as NaN bytes: anything the library reads
+    # without having written it, or fails to write, shows up as NaN
+    p = G.Prefill(q, k, v, cu_seqlens=cu, seqlen=inp.dense_T if inp.dense_T else None, num_seqs=inp.num_seqs,
+                  chunk_size=chunk or inp.chunk_size, heads_tiled=heads_tiled,
+                  scale=inp.scale if scale is None else scale, l2norm=l2norm)
+    p.ws.fill_(-1)
+    n, hv, dv = v.shape
+    o = torch.full((n, hv, dv), float("nan"), dtype=q.dtype, device=q.device)
+    S = torch.full((inp.num_seqs, hv, q.shape[2], dv), float("nan"), dtype=torch.float32, device=q.device)
+    p(q, k, v, to_dev(inp.g), to_dev(inp.beta), o, s0, S)
     torch.cuda.synchronize()
     return to_np(o), to_np(S)
 
