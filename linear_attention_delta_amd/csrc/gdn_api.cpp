@@ -3,6 +3,7 @@
 // the host before any HIP call, so an invalid call queues nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -103,10 +104,36 @@ int64_t max_chunks(const gdn_dims* d) {
   return (int64_t)d->total_tokens / C + d->num_seqs;
 }
 
+// Segment-parallel carry (bf16 operands, chunk 32 or 64): the library's
+// choice of segment length, in chunks.  About one segment per compute unit
+// for a single long sequence (the prefill then has 8 + (segments - 1) + 8
+// dependent chunk steps instead of 64); for batches that already fill the
+// GPU the segments grow so the extra carry of pass 1 stays small.
+bool seg_enabled(const gdn_dims* d) {
+  return d->dtype == GDN_BF16 && (d->chunk_size == 32 || d->chunk_size == 64);
+}
+
+int seg_len(const gdn_dims* d) {
+  const int64_t units = max_chunks(d) * d->num_v_heads;
+  return (int)std::max<int64_t>(8, (units + 255) / 256);
+}
+
+int64_t max_segs(const gdn_dims* d) {
+  const int64_t L = seg_len(d);
+  if (d->seqlen > 0) {
+    const int64_t cps = (d->seqlen + d->chunk_size - 1) / d->chunk_size;
+    return (int64_t)d->num_seqs * std::max<int64_t>(1, (cps + L - 1) / L);
+  }
+  return max_chunks(d) / L + d->num_seqs;
+}
+
 // Workspace: [chunk table (varlen only)] [Tt, P per chunk and v-head]
-// [a, b, c, e^{gamma_last} per chunk and v-head], each part 256-byte aligned.
+// [a, b, c, e^{gamma_last} per chunk and v-head], and on the segment path
+// [segment table (varlen only)] [segment start states, fp32]
+// [segment transitions, bf16]; each part 256-byte aligned.
 struct WsLayout {
-  size_t table_off, table_bytes, mats_off, mats_bytes, scal_off, scal_bytes, total;
+  size_t table_off, table_bytes, mats_off, mats_bytes, scal_off, scal_bytes;
+  size_t segt_off, segt_bytes, sst_off, sst_bytes, phi_off, phi_bytes, total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -121,7 +148,17 @@ WsLayout ws_layout(const gdn_dims* d) {
   w.mats_bytes = align256(units * 2 * C * C * elem_size(d->dtype));
   w.scal_off = w.mats_off + w.mats_bytes;
   w.scal_bytes = align256(units * 4 * C * 4);
-  w.total = w.scal_off + w.scal_bytes;
+  w.segt_off = w.scal_off + w.scal_bytes;
+  w.segt_bytes = w.sst_bytes = w.phi_bytes = 0;
+  if (seg_enabled(d)) {
+    const size_t segs = (size_t)max_segs(d) * d->num_v_heads;
+    w.segt_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1) * 4);
+    w.sst_bytes = align256(segs * d->head_dim_k * d->head_dim_v * 4);
+    w.phi_bytes = align256(segs * d->head_dim_k * d->head_dim_k * 2);
+  }
+  w.sst_off = w.segt_off + w.segt_bytes;
+  w.phi_off = w.sst_off + w.sst_bytes;
+  w.total = w.phi_off + w.phi_bytes;
   return w;
 }
 
@@ -197,6 +234,13 @@ void carve(gdn::ScanArgs& a, const gdn_dims* d, const void* ws) {
   a.tinv = base ? base + L.mats_off : nullptr;
   a.scal = base ? reinterpret_cast<float*>(base + L.scal_off) : nullptr;
   a.max_chunks = (int)max_chunks(d);
+  if (seg_enabled(d)) {
+    a.seg_len = seg_len(d);
+    a.max_segs = (int)max_segs(d);
+    a.seg_offsets = L.segt_bytes ? reinterpret_cast<int32_t*>(base + L.segt_off) : nullptr;
+    a.seg_state = base ? reinterpret_cast<float*>(base + L.sst_off) : nullptr;
+    a.seg_phi = base ? reinterpret_cast<uint16_t*>(base + L.phi_off) : nullptr;
+  }
 }
 
 gdn_status run_prepare(gdn::ScanArgs& a, hipStream_t s) {

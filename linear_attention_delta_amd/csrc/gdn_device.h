@@ -166,4 +166,50 @@ __device__ __forceinline__ float exp_cw(float x) {
   return x != x ? x : e;
 }
 
+// ------------------------------------------------- MFMA fragment helpers
+//
+// A 16x16 fp32 accumulator tile (lane (c, g) holds rows 4g..4g+3 of column
+// c) becomes half of a bf16 operand fragment when packed: two stacked tiles
+// give, per lane, the 8 values at k = {4g+e} and {16+4g+e} of one 32-wide
+// k step.  The other operand, read from LDS, must present the same k order;
+// LDS copies of row-major operands therefore store each 32-column block with
+// logical column 4g+e at 8g+e and 16+4g+e at 8g+4+e (perm_lo below), so a
+// fragment is one 16-byte read.
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__device__ __forceinline__ u32x2 pack4_bf16(f32x4 v) { return u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])}; }
+
+__device__ __forceinline__ bf16x8 frag2(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Operand fragment from two stacked accumulator tiles.
+__device__ __forceinline__ bf16x8 frag_acc(f32x4 lo, f32x4 hi) { return frag2(pack4_bf16(lo), pack4_bf16(hi)); }
+
+__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane L supplies the address of 4 consecutive bf16; lane i receives element
+// i % 4 of the loads of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.  With
+// lane L pointing at row r0 + L / 4, column c0 + 4 (L % 4) of a row-major
+// tile, lane i gets rows r0..r0+3 of column c0 + i.
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ f32x4 bf4_to_f32(u32x2 w) {
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+// Position in the LDS operand layout of the first 4 of the 8 logical columns
+// 8v..8v+7 (the other 4 go 8 further on).
+__device__ __forceinline__ int perm_lo(int v) { return 32 * (v >> 2) + 16 * (v & 1) + 4 * ((v >> 1) & 1); }
+
 }  // namespace gdn

@@ -43,6 +43,13 @@ struct ScanArgs {
   void* tinv;                 // [max_chunks][hv][2][chunk][chunk] in the operand type: Tt, P
   float* scal;                // [max_chunks][hv][4][chunk] fp32: a, b, c, e^{gamma_last}
   int max_chunks;
+  // segment-parallel scan (bf16, chunk 32/64): every sequence is cut into
+  // segments of seg_len chunks (at least one segment per sequence)
+  int seg_len;
+  int max_segs;               // bound on the number of segments, all sequences
+  int32_t* seg_offsets;       // [num_seqs + 1], varlen only
+  float* seg_state;           // [max_segs][hv][dk][dv] fp32: start state of each segment
+  uint16_t* seg_phi;          // [max_segs][hv][dk][dk] bf16: transition of each segment
   // decode only
   float* state;
   const int32_t* state_slots;
@@ -53,6 +60,9 @@ hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_chunk_table(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prepare(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+// true if launch_scan takes the segment-parallel path for these arguments
+bool seg_path(const ScanArgs& a);
+hipError_t launch_seg(const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(const ScanArgs& a, hipStream_t s);
 // GDN_DEBUG: count non-finite values (fp32 or bf16) into *count (device int).
 hipError_t launch_nonfinite_probe(const void* p, long n, int dtype, int* count, hipStream_t s);

@@ -40,34 +40,48 @@ namespace {
 constexpr float kL2Eps = 1e-6f;
 
 // ------------------------------------------------------------ chunk table
-// chunk_offsets[i] = sum_{j<i} ceil(len_j / C).  One workgroup; sequential
-// over blocks of 1024 sequences, scan inside a block.
+// chunk_offsets[i] = sum_{j<i} ceil(len_j / C), and for the segment-parallel
+// path seg_offsets[i] = sum_{j<i} max(1, ceil(ceil(len_j / C) / seg_len)).
+// One workgroup; sequential over blocks of 1024 sequences, scan inside a block.
 __global__ void __launch_bounds__(1024) k_chunk_table(ScanArgs a) {
-  __shared__ int carry;
-  __shared__ int buf[1024];
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ int carry[2];
+  __shared__ int buf[2][1024];
+  if (threadIdx.x < 2) carry[threadIdx.x] = 0;
   __syncthreads();
   for (int base = 0; base < a.num_seqs; base += 1024) {
     const int i = base + threadIdx.x;
-    int n = 0;
+    int n = 0, ns = 0;
     if (i < a.num_seqs) {
       const int len = a.cu_seqlens[i + 1] - a.cu_seqlens[i];
       n = (len + a.chunk - 1) / a.chunk;
+      if (a.seg_offsets) ns = n > 0 ? (n + a.seg_len - 1) / a.seg_len : 1;
     }
-    buf[threadIdx.x] = n;
+    buf[0][threadIdx.x] = n;
+    buf[1][threadIdx.x] = ns;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      int v = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scans
+      const int v0 = threadIdx.x >= off ? buf[0][threadIdx.x - off] : 0;
+      const int v1 = threadIdx.x >= off ? buf[1][threadIdx.x - off] : 0;
       __syncthreads();
-      buf[threadIdx.x] += v;
+      buf[0][threadIdx.x] += v0;
+      buf[1][threadIdx.x] += v1;
       __syncthreads();
     }
-    if (i < a.num_seqs) a.chunk_offsets[i + 1] = carry + buf[threadIdx.x];
+    if (i < a.num_seqs) {
+      a.chunk_offsets[i + 1] = carry[0] + buf[0][threadIdx.x];
+      if (a.seg_offsets) a.seg_offsets[i + 1] = carry[1] + buf[1][threadIdx.x];
+    }
     __syncthreads();
-    if (threadIdx.x == 1023) carry += buf[1023];
+    if (threadIdx.x == 1023) {
+      carry[0] += buf[0][1023];
+      carry[1] += buf[1][1023];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.chunk_offsets[0] = 0;
+  if (threadIdx.x == 0) {
+    a.chunk_offsets[0] = 0;
+    if (a.seg_offsets) a.seg_offsets[0] = 0;
+  }
 }
 
 // Locate global chunk n: its sequence, first token and length.  false if
@@ -516,7 +530,6 @@ __device__ __forceinline__ void st4(uint16_t* p, f32x4 v) {
 }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 template <class E, int C, int DK, int NT, bool DB>
 __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
@@ -779,36 +792,6 @@ struct alignas(16) ScanSmemBF {
   uint32_t hu[2][64][NRT * 2 + 4];     // U handoff: per lane NRT tiles x 4 bf16
 };
 
-__device__ __forceinline__ u32x2 pack4_bf16(f32x4 v) { return u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])}; }
-
-__device__ __forceinline__ bf16x8 frag2(u32x2 lo, u32x2 hi) {
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane L supplies the address of 4 consecutive bf16; lane i receives element
-// i % 4 of the loads of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.  With
-// lane L pointing at row r0 + L / 4, column c0 + 4 (L % 4) of a row-major
-// tile, lane i gets rows r0..r0+3 of column c0 + i.
-__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-__device__ __forceinline__ f32x4 bf4_to_f32(u32x2 w) {
-  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
-               __uint_as_float(w[1] & 0xffff0000u)};
-}
-
-// Position in the LDS operand layout of the first 4 of the 8 logical columns
-// 8v..8v+7 (the other 4 go 8 further on).
-__device__ __forceinline__ int perm_lo(int v) { return 32 * (v >> 2) + 16 * (v & 1) + 4 * ((v >> 1) & 1); }
 
 template <int C, int DK>
 __global__ void __launch_bounds__(512) k_scan_bf16(ScanArgs a) {
@@ -1190,6 +1173,7 @@ hipError_t launch_prepare(const ScanArgs& a, hipStream_t s) {
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.num_seqs == 0) return hipSuccess;
+  if (seg_path(a)) return launch_seg(a, s);
   return a.dtype == 1 ? dispatch_scan<BF16>(a, s) : dispatch_scan<F32>(a, s);
 }
 

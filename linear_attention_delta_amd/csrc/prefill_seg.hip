@@ -1,0 +1,662 @@
+// prefill_seg.hip -- segment-parallel carry of the chunked prefill (bf16
+// operands, chunk 32 or 64) on gfx950.
+//
+// Per chunk the state obeys the affine recurrence (notation of prefill.hip)
+//
+//   S' = e^{gamma_last} S + K^T diag(c) Tt (V - diag(a) K S)  =  M S + B,
+//
+// with M = e^{gamma_last} I - K^T diag(c) Tt diag(a) K independent of the
+// state.  The oxydllm 0.0.0-alpha.12.2 notes ("Performance", Gated DeltaNet
+// fast paths) make the cross-chunk loop cheap by precomputing everything
+// state-independent in batch; the loop itself stays sequential.  With one
+// sequence that loop is 64 chunks deep per head, far too little parallel
+// work for 256 compute units, so every sequence is cut into segments of
+// seg_len chunks and the carry runs in three launches:
+//
+//   pass 1  (one workgroup per segment and v-head, all but the last segment
+//           of a sequence) carries Z = [S | Phi] through the segment: S from
+//           zero (the true initial state for the first segment) and Phi from
+//           the identity, i.e. the segment's B and its transition
+//           Phi = M_last ... M_first.  Both go to the workspace.
+//   combine (one workgroup per sequence, v-head and 16 state columns) chains
+//           the segment starts: S_start[p+1] = Phi_p S_start[p] + B_p.
+//   pass 2  (one workgroup per segment and v-head) re-runs each segment from
+//           its true start state and writes the outputs
+//           O = diag(b) Q S + P U, and the final state.
+//
+// A workgroup holds a whole head (all d_v columns), so every chunk's K, Q,
+// V, Tt and P are staged into LDS once per pass, not once per column tile.
+// Four waves split the state columns; each keeps its slice of S (and Phi)
+// in fp32 MFMA accumulators for the whole segment and feeds it back as bf16
+// operands (gdn_device.h, MFMA fragment helpers).  Loads of chunk i+2 are in
+// flight while chunk i is computed; LDS is double-buffered with one barrier
+// per chunk.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+__device__ __forceinline__ int nseg_of(int nchunks, int L) { return nchunks > 0 ? (nchunks + L - 1) / L : 1; }
+
+struct Seg {
+  int seq, p, nseg;   // sequence, segment index in it, its segment count
+  int s0, s1;         // token range of the sequence
+  int cbase, sbase;   // first global chunk and first global segment of the sequence
+};
+
+// Global segment n (grids are sized by a bound: seq == -1 past the last one).
+__device__ __forceinline__ Seg seg_of(const ScanArgs& a, int C, int n) {
+  Seg g;
+  if (a.seqlen > 0) {
+    const int cps = (a.seqlen + C - 1) / C;
+    const int ns = nseg_of(cps, a.seg_len);
+    const int seq = n / ns;
+    g.seq = seq < a.num_seqs ? seq : -1;
+    g.p = n - seq * ns;
+    g.nseg = ns;
+    g.s0 = seq * a.seqlen;
+    g.s1 = g.s0 + a.seqlen;
+    g.cbase = seq * cps;
+    g.sbase = seq * ns;
+    return g;
+  }
+  const int total = a.seg_offsets[a.num_seqs];
+  int lo = 0, hi = a.num_seqs - 1;  // last sequence with seg_offsets[seq] <= n
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.seg_offsets[mid] <= n) lo = mid; else hi = mid - 1;
+  }
+  g.seq = n < total ? lo : -1;
+  g.sbase = a.seg_offsets[lo];
+  g.p = n - g.sbase;
+  g.nseg = a.seg_offsets[lo + 1] - g.sbase;
+  g.s0 = a.cu_seqlens[lo];
+  g.s1 = a.cu_seqlens[lo + 1];
+  g.cbase = a.chunk_offsets[lo];
+  return g;
+}
+
+// Block -> (global segment, v-head).  The G v-heads reading one q/k head in
+// one segment get the same blockIdx % 8, i.e. the same XCD, and share its L2
+// for K and Q.
+__device__ __forceinline__ void block_unit(const ScanArgs& a, int& n, int& hk, int& h) {
+  const int G = a.hv / a.hk;
+  const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
+  const int grp = (m8 / G) * 8 + xcd;
+  const int vh = m8 % G;
+  n = grp / a.hk;
+  hk = grp % a.hk;
+  h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) { return (uint16_t)(cvt_bf16x2(x, 0.f) & 0xffffu); }
+
+// Workspace images of segment data, laid out as the registers that use them
+// so that every access is one 16-byte word per lane:
+//  - a d_k x d_v fp32 state in accumulator form: tile (u, jt) (rows 16u..,
+//    columns 16jt..) is 64 lanes x f32x4, lane (c, g) holding rows 16u+4g+e
+//    of column 16jt+c;
+//  - a d_k x d_k bf16 transition as matrix-core A operands: fragment (u, m)
+//    (rows 16u.., k = 32m..) is 64 lanes x 8 bf16, lane (c, g) holding row
+//    16u+c at k = 32m + {4g+e, 16+4g+e}.
+template <int DV>
+__device__ __forceinline__ long state_frag(int u, int jt, int lane) {
+  return ((long)(u * (DV / 16) + jt) * 64 + lane) * 4;
+}
+template <int DK>
+__device__ __forceinline__ long phi_frag(int u, int m, int lane) {
+  return ((long)(u * (DK / 32) + m) * 64 + lane) * 8;
+}
+
+// LDS image of one chunk.  K and Q (and Tt, P) rows are stored with the
+// column permutation of perm_lo, V rows as they are.
+template <int C, int DK, int DV, bool OUT>
+struct alignas(16) SegSmem {
+  static constexpr int KLD = DK + 16;  // row pads keep 16-byte fragment reads conflict-free
+  static constexpr int VLD = DV + 16;
+  static constexpr int CLD = C + 8;
+  uint16_t k[2][C][KLD];
+  uint16_t v[2][C][VLD];
+  uint16_t tt[2][C][CLD];
+  float sc[2][4][C];                   // a, b, c, e^{gamma_last}
+  uint16_t q[OUT ? 2 : 1][OUT ? C : 1][KLD];
+  uint16_t p[OUT ? 2 : 1][OUT ? C : 1][CLD];
+};
+
+// Global -> register -> LDS staging of one chunk by the NTH threads of a
+// workgroup.  Rows of K, Q, V past the end of the sequence read as zero.
+template <int C, int DK, int DV, bool OUT, int NTH>
+struct Stager {
+  typedef SegSmem<C, DK, DV, OUT> SM;
+  static constexpr int KV = C * DK / 8, VV = C * DV / 8, TV = C * C / 8;  // 16-byte vectors
+  static constexpr int NK = (KV + NTH - 1) / NTH, NV = (VV + NTH - 1) / NTH, NT = (TV + NTH - 1) / NTH;
+  u32x4 rk[NK], rq[OUT ? NK : 1], rv[NV], rt[NT], rp[OUT ? NT : 1], rs;
+  float rbq[OUT ? NK : 1];  // b of each staged Q row: Q is stored as diag(b) Q
+  const uint16_t *kp, *qp, *vp, *mp;
+  const float* sp;
+  long sk, sq, sv, mstep, sstep;
+  int ntok, tid;
+
+  __device__ __forceinline__ void load(int ch) {  // ch: chunk index within the sequence
+    const int cs = ch * C;
+    const int clen = min(C, ntok - cs);
+#pragma unroll
+    for (int j = 0; j < NK; j++) {
+      const int idx = tid + NTH * j, r = idx / (DK / 8), cv = idx % (DK / 8);
+      const bool ok = idx < KV && r < clen;
+      rk[j] = ok ? *reinterpret_cast<const u32x4*>(kp + (long)(cs + r) * sk + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (OUT) {
+        rq[j] = ok ? *reinterpret_cast<const u32x4*>(qp + (long)(cs + r) * sq + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
+        rbq[j] = idx < KV ? sp[ch * sstep + C + r] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + NTH * j, r = idx / (DV / 8), cv = idx % (DV / 8);
+      rv[j] = (idx < VV && r < clen) ? *reinterpret_cast<const u32x4*>(vp + (long)(cs + r) * sv + 8 * cv)
+                                     : u32x4{0u, 0u, 0u, 0u};
+    }
+    const uint16_t* mc = mp + ch * mstep;
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+      const int idx = tid + NTH * j;
+      if (idx < TV) {
+        rt[j] = *reinterpret_cast<const u32x4*>(mc + 8 * idx);
+        if constexpr (OUT) rp[j] = *reinterpret_cast<const u32x4*>(mc + C * C + 8 * idx);
+      }
+    }
+    if (tid < C) rs = *reinterpret_cast<const u32x4*>(sp + ch * sstep + 4 * tid);
+  }
+
+  __device__ __forceinline__ void store(SM& sm, int b) const {
+#pragma unroll
+    for (int j = 0; j < NK; j++) {
+      const int idx = tid + NTH * j, r = idx / (DK / 8), lo = perm_lo(idx % (DK / 8));
+      if (idx < KV) {
+        *reinterpret_cast<u32x2*>(&sm.k[b][r][lo]) = u32x2{rk[j][0], rk[j][1]};
+        *reinterpret_cast<u32x2*>(&sm.k[b][r][lo + 8]) = u32x2{rk[j][2], rk[j][3]};
+        if constexpr (OUT) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            w[e] = cvt_bf16x2(rbq[j] * __uint_as_float(rq[j][e] << 16), rbq[j] * __uint_as_float(rq[j][e] & 0xffff0000u));
+          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo]) = u32x2{w[0], w[1]};
+          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo + 8]) = u32x2{w[2], w[3]};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + NTH * j, r = idx / (DV / 8), cv = idx % (DV / 8);
+      if (idx < VV) *reinterpret_cast<u32x4*>(&sm.v[b][r][8 * cv]) = rv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+      const int idx = tid + NTH * j, r = idx / (C / 8), lo = perm_lo(idx % (C / 8));
+      if (idx < TV) {
+        *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo]) = u32x2{rt[j][0], rt[j][1]};
+        *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo + 8]) = u32x2{rt[j][2], rt[j][3]};
+        if constexpr (OUT) {
+          *reinterpret_cast<u32x2*>(&sm.p[b][r][lo]) = u32x2{rp[j][0], rp[j][1]};
+          *reinterpret_cast<u32x2*>(&sm.p[b][r][lo + 8]) = u32x2{rp[j][2], rp[j][3]};
+        }
+      }
+    }
+    if (tid < C) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + 4 * tid) = rs;
+  }
+};
+
+// One chunk of the carry for the NCT 16-column tiles of Z owned by this
+// wave (tile j is state column tile col[j]; vcol[j] < 0 marks a transition
+// tile, whose values term is zero).  Z <- e^{gl} Z + K^T diag(c) Tt (V -
+// diag(a) K Z).  With OUT, also O^T = Z^T (diag(b) Q)^T + U^T P^T (the staged Q
+// rows already carry b), returned in
+// ob as bf16: lane (c16, g) holds columns 4g..4g+3 of tile j for token 16t+c16.
+template <int C, int DK, int DV, int NCT, bool OUT>
+__device__ __forceinline__ void carry_chunk(SegSmem<C, DK, DV, OUT>& sm, int b, f32x4 (&Z)[DK / 16][NCT],
+                                            const int (&vcol)[NCT], int lane, u32x2 (&ob)[NCT][C / 16]) {
+  typedef SegSmem<C, DK, DV, OUT> SM;
+  constexpr int NRT = C / 16, PS = C / 32, KS = DK / 32, NDT = DK / 16;
+  const int c16 = lane & 15, g = lane >> 4, r4 = 4 * g;
+
+  // Z as bf16 operand fragments, k = d_k rows 32m + {4g+e, 16+4g+e}
+  bf16x8 zb[KS][NCT];
+#pragma unroll
+  for (int m = 0; m < KS; m++)
+#pragma unroll
+    for (int j = 0; j < NCT; j++) zb[m][j] = frag_acc(Z[2 * m][j], Z[2 * m + 1][j]);
+
+  // X = K Z
+  f32x4 X[NRT][NCT];
+#pragma unroll
+  for (int t = 0; t < NRT; t++)
+#pragma unroll
+    for (int j = 0; j < NCT; j++) X[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < KS; m++)
+#pragma unroll
+    for (int t = 0; t < NRT; t++) {
+      const bf16x8 ak = ld_frag(&sm.k[b][16 * t + c16][32 * m + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < NCT; j++) X[t][j] = mfma16(ak, zb[m][j], X[t][j]);
+    }
+
+  // R = V - diag(a) X  (lane: tokens 16t + 4g + e of column c16 of the tile)
+#pragma unroll
+  for (int t = 0; t < NRT; t++) {
+    const f32x4 av = ld4(&sm.sc[b][0][16 * t + r4]);
+#pragma unroll
+    for (int j = 0; j < NCT; j++) {
+      f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+      if (vcol[j] >= 0) vv = bf4_to_f32(ld_tr(&sm.v[b][16 * t + r4 + (c16 >> 2)][vcol[j] + 4 * (c16 & 3)]));
+      X[t][j] = vv - av * X[t][j];
+    }
+  }
+
+  // U = Tt R (Tt lower triangular by 16-row blocks: row tile t needs k steps pp <= t/2)
+  f32x4 U[NRT][NCT];
+#pragma unroll
+  for (int t = 0; t < NRT; t++)
+#pragma unroll
+    for (int j = 0; j < NCT; j++) U[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pp = 0; pp < PS; pp++) {
+    bf16x8 rb[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; j++) rb[j] = frag_acc(X[2 * pp][j], X[2 * pp + 1][j]);
+#pragma unroll
+    for (int t = 2 * pp; t < NRT; t++) {
+      const bf16x8 at = ld_frag(&sm.tt[b][16 * t + c16][32 * pp + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < NCT; j++) U[t][j] = mfma16(at, rb[j], U[t][j]);
+    }
+  }
+
+  if constexpr (OUT) {
+    // O^T = Z^T (diag(b) Q)^T + U^T P^T; lane (c16, g) holds 4 consecutive
+    // columns 4g..4g+3 of token 16t + c16
+    f32x4 Y[NCT][NRT];
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int t = 0; t < NRT; t++) Y[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KS; m++)
+#pragma unroll
+      for (int t = 0; t < NRT; t++) {
+        const bf16x8 bq = ld_frag(&sm.q[b][16 * t + c16][32 * m + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < NCT; j++) Y[j][t] = mfma16(zb[m][j], bq, Y[j][t]);
+      }
+#pragma unroll
+    for (int pp = 0; pp < PS; pp++) {
+      bf16x8 ub[NCT];
+#pragma unroll
+      for (int j = 0; j < NCT; j++) ub[j] = frag_acc(U[2 * pp][j], U[2 * pp + 1][j]);
+#pragma unroll
+      for (int t = 2 * pp; t < NRT; t++) {
+        const bf16x8 bp = ld_frag(&sm.p[b][16 * t + c16][32 * pp + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < NCT; j++) Y[j][t] = mfma16(ub[j], bp, Y[j][t]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int t = 0; t < NRT; t++) ob[j][t] = pack4_bf16(Y[j][t]);
+  }
+
+  // Z <- e^{gamma_last} Z + K^T (diag(c) U)
+#pragma unroll
+  for (int t = 0; t < NRT; t++) {
+    const f32x4 cv = ld4(&sm.sc[b][2][16 * t + r4]);
+#pragma unroll
+    for (int j = 0; j < NCT; j++) U[t][j] = cv * U[t][j];
+  }
+  const float gl = sm.sc[b][3][0];
+#pragma unroll
+  for (int u = 0; u < NDT; u++)
+#pragma unroll
+    for (int j = 0; j < NCT; j++) Z[u][j] = gl * Z[u][j];
+#pragma unroll
+  for (int pp = 0; pp < PS; pp++) {
+    bf16x8 ub[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; j++) ub[j] = frag_acc(U[2 * pp][j], U[2 * pp + 1][j]);
+#pragma unroll
+    for (int u = 0; u < NDT; u++) {
+      // K^T fragment: lane (c16, g) gets K[32pp + {4g+e, 16+4g+e}][16u + c16]
+      const uint16_t* p0 = &sm.k[b][32 * pp + r4 + (c16 >> 2)][32 * (u >> 1) + 8 * (c16 & 3) + 4 * (u & 1)];
+      const bf16x8 akt = frag2(ld_tr(p0), ld_tr(p0 + 16 * SM::KLD));
+#pragma unroll
+      for (int j = 0; j < NCT; j++) Z[u][j] = mfma16(akt, ub[j], Z[u][j]);
+    }
+  }
+}
+
+// Set up a stager for (segment g, heads hk / h).
+template <int C, int DK, int DV, bool OUT, int NTH>
+__device__ __forceinline__ void init_stager(Stager<C, DK, DV, OUT, NTH>& st, const ScanArgs& a, const Seg& sg, int hk,
+                                            int h, int tid) {
+  st.tid = tid;
+  st.ntok = sg.s1 - sg.s0;
+  st.sk = a.stride_k;
+  st.sq = a.stride_q;
+  st.sv = a.stride_v;
+  st.kp = reinterpret_cast<const uint16_t*>(a.k) + (long)sg.s0 * a.stride_k + (long)hk * DK;
+  st.qp = reinterpret_cast<const uint16_t*>(a.q) + (long)sg.s0 * a.stride_q + (long)hk * DK;
+  st.vp = reinterpret_cast<const uint16_t*>(a.v) + (long)sg.s0 * a.stride_v + (long)h * DV;
+  st.mp = reinterpret_cast<const uint16_t*>(a.tinv) + ((long)sg.cbase * a.hv + h) * (2 * C * C);
+  st.sp = a.scal + ((long)sg.cbase * a.hv + h) * (4 * C);
+  st.mstep = (long)a.hv * (2 * C * C);
+  st.sstep = (long)a.hv * (4 * C);
+}
+
+// ------------------------------------------------------------------ pass 1
+template <int C, int DK, int DV, int NW>
+__global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
+  typedef SegSmem<C, DK, DV, false> SM;
+  constexpr int NDT = DK / 16;
+  constexpr int NCT = (DV + DK) / (16 * NW);  // [S | Phi] column tiles per wave
+  constexpr int SVT = DV / 16;                // tiles below SVT are state columns
+  static_assert(NCT * 16 * NW == DV + DK, "columns must split over the waves");
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, r4 = 4 * (lane >> 4);
+  int n, hk, h;
+  block_unit(a, n, hk, h);
+  const Seg sg = seg_of(a, C, n);
+  if (sg.seq < 0 || sg.p >= sg.nseg - 1) return;  // the last segment needs no carry pass
+  const int ch0 = sg.p * a.seg_len;
+  const int nch = a.seg_len;  // every segment but the last is full
+
+  int vcol[NCT];
+  f32x4 Z[NDT][NCT];
+  const float* sin = (sg.p == 0 && a.state_in) ? a.state_in + ((long)sg.seq * a.hv + h) * DK * DV : nullptr;
+  float* sst = a.seg_state + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DV;
+#pragma unroll
+  for (int j = 0; j < NCT; j++) {
+    const int gt = wave * NCT + j;
+    vcol[j] = gt < SVT ? 16 * gt : -1;
+    const int col = gt < SVT ? 16 * gt + c16 : 16 * (gt - SVT) + c16;
+#pragma unroll
+    for (int u = 0; u < NDT; u++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int row = 16 * u + r4 + e;
+        if (gt < SVT) Z[u][j][e] = sin ? sin[(long)row * DV + col] : 0.f;
+        else Z[u][j][e] = row == col ? 1.f : 0.f;
+      }
+      // the first segment records its start state for pass 2 (the caller's
+      // state_in may be overwritten by state_out meanwhile)
+      if (sg.p == 0 && gt < SVT) *reinterpret_cast<f32x4*>(sst + state_frag<DV>(u, gt, lane)) = Z[u][j];
+    }
+  }
+
+  Stager<C, DK, DV, false, 64 * NW> st;
+  init_stager(st, a, sg, hk, h, tid);
+  st.load(ch0);
+  st.store(sm, 0);
+  if (nch > 1) st.load(ch0 + 1);
+  u32x2 ob[NCT][C / 16];
+  for (int i = 0; i < nch; i++) {
+    __syncthreads();
+    const int b = i & 1;
+    if (i + 1 < nch) st.store(sm, b ^ 1);
+    if (i + 2 < nch) st.load(ch0 + i + 2);
+    carry_chunk<C, DK, DV, NCT, false>(sm, b, Z, vcol, lane, ob);
+  }
+
+  // B_p (or the true end state of the first segment) is the next segment's
+  // start before the combine
+  float* snext = sst + (long)a.hv * DK * DV;
+#pragma unroll
+  for (int j = 0; j < NCT; j++) {
+    const int gt = wave * NCT + j;
+    if (gt < SVT) {
+#pragma unroll
+      for (int u = 0; u < NDT; u++) *reinterpret_cast<f32x4*>(snext + state_frag<DV>(u, gt, lane)) = Z[u][j];
+    }
+  }
+  if (sg.p == 0) return;
+  // Phi_p in bf16 as A-operand fragments: transposed through LDS (the chunk
+  // buffers are free once every wave is past the last chunk)
+  constexpr int PLD = DK + 8;
+  uint16_t* img = reinterpret_cast<uint16_t*>(&sm);
+  static_assert(sizeof(SM) >= DK * PLD * 2, "transition image must fit the chunk buffers");
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NCT; j++) {
+    const int gt = wave * NCT + j;
+    if (gt >= SVT) {
+#pragma unroll
+      for (int u = 0; u < NDT; u++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) img[(16 * u + r4 + e) * PLD + 16 * (gt - SVT) + c16] = bf16_rne(Z[u][j][e]);
+    }
+  }
+  __syncthreads();
+  uint16_t* phi = a.seg_phi + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DK;
+  for (int f = wave; f < NDT * (DK / 32); f += NW) {
+    const int u = f / (DK / 32), m = f % (DK / 32);
+    const uint16_t* row = img + (16 * u + c16) * PLD + 32 * m + r4;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(row), hi = *reinterpret_cast<const u32x2*>(row + 16);
+    *reinterpret_cast<u32x4*>(phi + phi_frag<DK>(u, m, lane)) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// ----------------------------------------------------------------- combine
+// One workgroup per (sequence, v-head); wave w owns state columns
+// 16 NCT w .. (all rows), so its slice of S feeds the matrix cores straight
+// from its accumulators.  S_start[p+1] = Phi_p S_start[p] + B_p for
+// p = 1 .. nseg-2, in place over B_p.  Phi_p is staged into LDS (shared by
+// the four waves); the loads of step p+1 are in flight during step p.
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) k_seg_combine(ScanArgs a) {
+  constexpr int NDT = DK / 16, KS = DK / 32, NJT = DV / 16, NCT = NJT / 4;
+  constexpr int PV = DK * DK / 8 / 256;  // 16-byte words of Phi per thread
+  static_assert(NCT >= 1 && NCT * 4 == NJT && PV * 256 * 8 == DK * DK, "shape");
+  __shared__ u32x4 phl[2][DK * DK / 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x % a.hv;
+  const int seq = blockIdx.x / a.hv;
+  if (seq >= a.num_seqs) return;
+  int nseg, sbase;
+  if (a.seqlen > 0) {
+    nseg = nseg_of((a.seqlen + a.chunk - 1) / a.chunk, a.seg_len);
+    sbase = seq * nseg;
+  } else {
+    sbase = a.seg_offsets[seq];
+    nseg = a.seg_offsets[seq + 1] - sbase;
+  }
+  if (nseg < 3) return;
+  auto sptr = [&](int p) { return a.seg_state + ((long)(sbase + p) * a.hv + h) * DK * DV; };
+  auto pptr = [&](int p) { return reinterpret_cast<const u32x4*>(a.seg_phi + ((long)(sbase + p) * a.hv + h) * DK * DK); };
+
+  f32x4 S[NDT][NCT];
+  {
+    const float* s1 = sptr(1);
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int j = 0; j < NCT; j++) S[u][j] = *reinterpret_cast<const f32x4*>(s1 + state_frag<DV>(u, wave * NCT + j, lane));
+  }
+  u32x4 pf[PV];
+  f32x4 bf[NDT][NCT];
+  auto load_step = [&](int p) {  // Phi_p and B_p (held in S_start[p+1])
+    const u32x4* ph = pptr(p);
+#pragma unroll
+    for (int i = 0; i < PV; i++) pf[i] = ph[tid + 256 * i];
+    const float* b = sptr(p + 1);
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int j = 0; j < NCT; j++) bf[u][j] = *reinterpret_cast<const f32x4*>(b + state_frag<DV>(u, wave * NCT + j, lane));
+  };
+  // S_start[p] (p >= 2) is written at the top of step p, after the wait for
+  // the step's loads and before the next loads are issued: waiting for loads
+  // then never waits for a fresh store to be acknowledged.
+  auto store_state = [&](int p) {
+    float* dst = sptr(p);
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int j = 0; j < NCT; j++) *reinterpret_cast<f32x4*>(dst + state_frag<DV>(u, wave * NCT + j, lane)) = S[u][j];
+  };
+  load_step(1);
+  for (int p = 1; p <= nseg - 2; p++) {
+    const int b = p & 1;
+#pragma unroll
+    for (int i = 0; i < PV; i++) phl[b][tid + 256 * i] = pf[i];
+    f32x4 acc[NDT][NCT];
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int j = 0; j < NCT; j++) acc[u][j] = bf[u][j];
+    if (p >= 2) store_state(p);
+    if (p + 1 <= nseg - 2) load_step(p + 1);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < KS; m++) {
+      bf16x8 zb[NCT];
+#pragma unroll
+      for (int j = 0; j < NCT; j++) zb[j] = frag_acc(S[2 * m][j], S[2 * m + 1][j]);
+#pragma unroll
+      for (int u = 0; u < NDT; u++) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, phl[b][(u * KS + m) * 64 + lane]);
+#pragma unroll
+        for (int j = 0; j < NCT; j++) acc[u][j] = mfma16(af, zb[j], acc[u][j]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NDT; u++)
+#pragma unroll
+      for (int j = 0; j < NCT; j++) S[u][j] = acc[u][j];
+  }
+  store_state(nseg - 1);
+}
+
+// ------------------------------------------------------------------ pass 2
+// Eight waves: 0..3 carry the state (NCT column tiles each) and write the
+// outputs, 4..7 stage the chunks.  The staging registers live only in the
+// staging waves, so the carry keeps its accumulators in VGPRs.
+template <int C, int DK, int DV>
+__global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
+  typedef SegSmem<C, DK, DV, true> SM;
+  constexpr int NDT = DK / 16;
+  constexpr int NCT = DV / 64;  // state column tiles per carry wave
+  static_assert(DV % 64 == 0, "state columns must split over four waves");
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, r4 = 4 * (lane >> 4);
+  int n, hk, h;
+  block_unit(a, n, hk, h);
+  const Seg sg = seg_of(a, C, n);
+  if (sg.seq < 0) return;
+  const int nch_seq = (sg.s1 - sg.s0 + C - 1) / C;
+  const int ch0 = sg.p * a.seg_len;
+  const int nch = max(0, min(a.seg_len, nch_seq - ch0));
+
+  if (wave >= 4) {
+    // staging: chunk i+1 is written to LDS and chunk i+2 requested while
+    // the carry waves work on chunk i
+    Stager<C, DK, DV, true, 256> st;
+    init_stager(st, a, sg, hk, h, tid - 256);
+    if (nch > 0) {
+      st.load(ch0);
+      st.store(sm, 0);
+      if (nch > 1) st.load(ch0 + 1);
+    }
+    for (int i = 0; i < nch; i++) {
+      __syncthreads();
+      if (i + 1 < nch) st.store(sm, (i + 1) & 1);
+      if (i + 2 < nch) st.load(ch0 + i + 2);
+    }
+    return;
+  }
+
+  int vcol[NCT];
+  f32x4 Z[NDT][NCT];
+  const float* sin = a.state_in ? a.state_in + ((long)sg.seq * a.hv + h) * DK * DV : nullptr;
+  const float* sws = a.seg_state + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DV;
+#pragma unroll
+  for (int j = 0; j < NCT; j++) {
+    vcol[j] = 16 * (wave * NCT + j);
+#pragma unroll
+    for (int u = 0; u < NDT; u++) {
+      if (sg.nseg > 1) {
+        Z[u][j] = *reinterpret_cast<const f32x4*>(sws + state_frag<DV>(u, wave * NCT + j, lane));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) Z[u][j][e] = sin ? sin[(long)(16 * u + r4 + e) * DV + vcol[j] + c16] : 0.f;
+      }
+    }
+  }
+  const long orow = (long)a.hv * DV;
+  uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)sg.s0 * orow + (long)h * DV;
+  u32x2 ob[NCT][C / 16];
+  for (int i = 0; i < nch; i++) {
+    __syncthreads();
+    carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob);
+    const int cs = (ch0 + i) * C;
+    const int clen = min(C, sg.s1 - sg.s0 - cs);
+    uint16_t* oc = obase + (long)cs * orow;
+#pragma unroll
+    for (int t = 0; t < C / 16; t++) {
+      const int tok = 16 * t + c16;
+      if (tok < clen) {
+#pragma unroll
+        for (int j = 0; j < NCT; j++) *reinterpret_cast<u32x2*>(oc + (long)tok * orow + vcol[j] + r4) = ob[j][t];
+      }
+    }
+  }
+
+  if (sg.p == sg.nseg - 1 && a.state_out) {
+    float* so = a.state_out + ((long)sg.seq * a.hv + h) * DK * DV;
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int u = 0; u < NDT; u++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) so[(long)(16 * u + r4 + e) * DV + vcol[j] + c16] = Z[u][j][e];
+  }
+}
+
+template <int C, int DK, int DV>
+hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
+  const int G = a.hv / a.hk;
+  const int groups = a.max_segs * a.hk;
+  const dim3 grid(8 * ((groups + 7) / 8) * G), block(256);
+  constexpr int NW1 = (DV + DK) % 128 == 0 ? 8 : 4;  // pass 1: 32 (or 48) columns per wave
+  hipLaunchKernelGGL((k_seg_pass1<C, DK, DV, NW1>), grid, dim3(64 * NW1), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_seg_combine<DK, DV>), dim3(a.num_seqs * a.hv), block, 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_seg_pass2<C, DK, DV>), grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_seg_c(const ScanArgs& a, hipStream_t s) {
+  if (a.dk == 128 && a.dv == 128) return launch_seg_t<C, 128, 128>(a, s);
+  if (a.dk == 128 && a.dv == 64) return launch_seg_t<C, 128, 64>(a, s);
+  if (a.dk == 64 && a.dv == 128) return launch_seg_t<C, 64, 128>(a, s);
+  if (a.dk == 64 && a.dv == 64) return launch_seg_t<C, 64, 64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool seg_path(const ScanArgs& a) {
+  return a.dtype == 1 && (a.chunk == 32 || a.chunk == 64) && (a.dk == 64 || a.dk == 128) &&
+         (a.dv == 64 || a.dv == 128);
+}
+
+hipError_t launch_seg(const ScanArgs& a, hipStream_t s) {
+  if (a.num_seqs == 0) return hipSuccess;
+  return a.chunk == 64 ? launch_seg_c<64>(a, s) : launch_seg_c<32>(a, s);
+}
+
+}  // namespace gdn
