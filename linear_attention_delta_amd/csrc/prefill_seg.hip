@@ -447,20 +447,26 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
 }
 
 // ----------------------------------------------------------------- combine
-// One workgroup per (sequence, v-head); wave w owns state columns
-// 16 NCT w .. (all rows), so its slice of S feeds the matrix cores straight
-// from its accumulators.  S_start[p+1] = Phi_p S_start[p] + B_p for
-// p = 1 .. nseg-2, in place over B_p.  Phi_p is staged into LDS (shared by
-// the four waves); the loads of step p+1 are in flight during step p.
+// S_start[p+1] = Phi_p S_start[p] + B_p for p = 1 .. nseg-2, in place over
+// B_p.  One workgroup per (sequence, v-head, 64 state columns), eight waves:
+//  - waves 0..3 each own one 16-column tile of S (all rows) in accumulators,
+//    so S feeds the matrix cores straight from registers; they only store;
+//  - waves 4..7 only load: Phi_p and the B_p columns, two steps ahead in two
+//    register sets, into a two-slot LDS ring.
+// Keeping loads and stores in different waves means no wait for a load ever
+// has to wait for a store to be acknowledged.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_seg_combine(ScanArgs a) {
-  constexpr int NDT = DK / 16, KS = DK / 32, NJT = DV / 16, NCT = NJT / 4;
-  constexpr int PV = DK * DK / 8 / 256;  // 16-byte words of Phi per thread
-  static_assert(NCT >= 1 && NCT * 4 == NJT && PV * 256 * 8 == DK * DK, "shape");
+__global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
+  constexpr int NDT = DK / 16, KS = DK / 32, NH = DV / 64;  // column halves of 64
+  constexpr int PV = DK * DK / 8 / 256;                    // 16-byte words of Phi per loader thread
+  constexpr int BV = NDT * 4 * 64 / 256;                   // f32x4 words of B per loader thread
+  static_assert(PV * 256 * 8 == DK * DK && BV * 256 == NDT * 4 * 64, "shape");
   __shared__ u32x4 phl[2][DK * DK / 8];
+  __shared__ f32x4 bl[2][NDT * 4 * 64];                     // [u][tile][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x % a.hv;
-  const int seq = blockIdx.x / a.hv;
+  const int half = blockIdx.x % NH;
+  const int h = (blockIdx.x / NH) % a.hv;
+  const int seq = blockIdx.x / (NH * a.hv);
   if (seq >= a.num_seqs) return;
   int nseg, sbase;
   if (a.seqlen > 0) {
@@ -471,70 +477,74 @@ __global__ void __launch_bounds__(256) k_seg_combine(ScanArgs a) {
     nseg = a.seg_offsets[seq + 1] - sbase;
   }
   if (nseg < 3) return;
+  const int last = nseg - 2;  // steps p = 1 .. last
   auto sptr = [&](int p) { return a.seg_state + ((long)(sbase + p) * a.hv + h) * DK * DV; };
-  auto pptr = [&](int p) { return reinterpret_cast<const u32x4*>(a.seg_phi + ((long)(sbase + p) * a.hv + h) * DK * DK); };
 
-  f32x4 S[NDT][NCT];
+  if (wave >= 4) {
+    const int lt = tid - 256;
+    struct Set {
+      u32x4 pf[PV];
+      f32x4 bf[BV];
+    } r0, r1;
+    auto load = [&](int p, Set& r) {  // Phi_p and B_p (held in S_start[p+1])
+      const u32x4* ph = reinterpret_cast<const u32x4*>(a.seg_phi + ((long)(sbase + p) * a.hv + h) * DK * DK);
+#pragma unroll
+      for (int i = 0; i < PV; i++) r.pf[i] = ph[lt + 256 * i];
+      const float* b = sptr(p + 1);
+#pragma unroll
+      for (int i = 0; i < BV; i++) {
+        const int w = lt + 256 * i, u = w / 256, t = (w / 64) % 4, l = w % 64;
+        r.bf[i] = *reinterpret_cast<const f32x4*>(b + state_frag<DV>(u, 4 * half + t, l));
+      }
+    };
+    auto put = [&](int p, Set& r) {
+#pragma unroll
+      for (int i = 0; i < PV; i++) phl[p & 1][lt + 256 * i] = r.pf[i];
+#pragma unroll
+      for (int i = 0; i < BV; i++) bl[p & 1][lt + 256 * i] = r.bf[i];
+    };
+    load(1, r0);
+    if (last >= 2) load(2, r1);
+    for (int p = 1; p <= last; p += 2) {
+      put(p, r0);
+      if (p + 2 <= last) load(p + 2, r0);
+      __syncthreads();
+      if (p + 1 <= last) {
+        put(p + 1, r1);
+        if (p + 3 <= last) load(p + 3, r1);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
+  const int jt = 4 * half + wave;  // this wave's column tile
+  f32x4 S[NDT];
   {
     const float* s1 = sptr(1);
 #pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int j = 0; j < NCT; j++) S[u][j] = *reinterpret_cast<const f32x4*>(s1 + state_frag<DV>(u, wave * NCT + j, lane));
+    for (int u = 0; u < NDT; u++) S[u] = *reinterpret_cast<const f32x4*>(s1 + state_frag<DV>(u, jt, lane));
   }
-  u32x4 pf[PV];
-  f32x4 bf[NDT][NCT];
-  auto load_step = [&](int p) {  // Phi_p and B_p (held in S_start[p+1])
-    const u32x4* ph = pptr(p);
-#pragma unroll
-    for (int i = 0; i < PV; i++) pf[i] = ph[tid + 256 * i];
-    const float* b = sptr(p + 1);
-#pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int j = 0; j < NCT; j++) bf[u][j] = *reinterpret_cast<const f32x4*>(b + state_frag<DV>(u, wave * NCT + j, lane));
-  };
-  // S_start[p] (p >= 2) is written at the top of step p, after the wait for
-  // the step's loads and before the next loads are issued: waiting for loads
-  // then never waits for a fresh store to be acknowledged.
-  auto store_state = [&](int p) {
-    float* dst = sptr(p);
-#pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int j = 0; j < NCT; j++) *reinterpret_cast<f32x4*>(dst + state_frag<DV>(u, wave * NCT + j, lane)) = S[u][j];
-  };
-  load_step(1);
-  for (int p = 1; p <= nseg - 2; p++) {
-    const int b = p & 1;
-#pragma unroll
-    for (int i = 0; i < PV; i++) phl[b][tid + 256 * i] = pf[i];
-    f32x4 acc[NDT][NCT];
-#pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int j = 0; j < NCT; j++) acc[u][j] = bf[u][j];
-    if (p >= 2) store_state(p);
-    if (p + 1 <= nseg - 2) load_step(p + 1);
+  for (int p = 1; p <= last; p++) {
     __syncthreads();
+    const int b = p & 1;
+    f32x4 acc[NDT];
+#pragma unroll
+    for (int u = 0; u < NDT; u++) acc[u] = bl[b][(u * 4 + wave) * 64 + lane];
 #pragma unroll
     for (int m = 0; m < KS; m++) {
-      bf16x8 zb[NCT];
+      const bf16x8 zb = frag_acc(S[2 * m], S[2 * m + 1]);
 #pragma unroll
-      for (int j = 0; j < NCT; j++) zb[j] = frag_acc(S[2 * m][j], S[2 * m + 1][j]);
-#pragma unroll
-      for (int u = 0; u < NDT; u++) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, phl[b][(u * KS + m) * 64 + lane]);
-#pragma unroll
-        for (int j = 0; j < NCT; j++) acc[u][j] = mfma16(af, zb[j], acc[u][j]);
-      }
+      for (int u = 0; u < NDT; u++)
+        acc[u] = mfma16(__builtin_bit_cast(bf16x8, phl[b][(u * KS + m) * 64 + lane]), zb, acc[u]);
     }
+    float* dst = sptr(p + 1);
 #pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int j = 0; j < NCT; j++) S[u][j] = acc[u][j];
+    for (int u = 0; u < NDT; u++) {
+      S[u] = acc[u];
+      *reinterpret_cast<f32x4*>(dst + state_frag<DV>(u, jt, lane)) = acc[u];
+    }
   }
-  store_state(nseg - 1);
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -632,7 +642,7 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_seg_pass1<C, DK, DV, NW1>), grid, dim3(64 * NW1), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_seg_combine<DK, DV>), dim3(a.num_seqs * a.hv), block, 0, s, a);
+  hipLaunchKernelGGL((k_seg_combine<DK, DV>), dim3(a.num_seqs * a.hv * (DV / 64)), dim3(512), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((k_seg_pass2<C, DK, DV>), grid, dim3(512), 0, s, a);
   return hipGetLastError();

@@ -138,3 +138,33 @@ def test_conv_special_values_bitexact(G, orc):
     got = _bits(y)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]:#06x} want {ref[tuple(bad[0])]:#06x}"
+
+
+def test_silu_bf16_pre_activation_sweep(G, orc):
+    """SiLU of chosen fp32 pre-activations, rounded to bf16, equals the
+    oracle's fp32 definition bit for bit.  A width-2 conv with taps
+    (a_c, 1) over the rows x = (1, 0) gives pre-activation exactly a_c at the
+    second token, so the sweep covers every bf16 value, a million random
+    fp32 values in [-12, 12] (about 0.05% of which land near a bf16 rounding
+    midpoint, where the kernel switches to the exact division), arbitrary
+    fp32 bit patterns (NaN, infinities, subnormals, large negatives)."""
+    import torch
+    note("conv SiLU pre-activation sweep bf16")
+    r = np.random.default_rng(12)
+    n_uni, n_bits = 1 << 20, 1 << 19
+    a = np.concatenate([
+        (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32),
+        r.uniform(-12.0, 12.0, n_uni).astype(np.float32),
+        r.integers(0, 1 << 32, n_bits, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ])
+    C = len(a)
+    assert C % 8 == 0
+    w = np.stack([a, np.ones_like(a)], axis=1).astype(np.float32)
+    x = np.zeros((2, C), dtype=np.float32)
+    x[0] = 1.0
+    y = G.conv1d(to_dev(x, "bf16"), torch.from_numpy(w).cuda(), seqlen=2)
+    torch.cuda.synchronize()
+    got = _bits(y)[1]
+    ref = orc.conv1d_f32(x, w, np.array([0, 2], dtype=np.int32), out_bf16=True)[1]
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} mismatches, first a={a[bad[0]]!r}: got {got[bad[0]]:#06x} want {ref[bad[0]]:#06x}"

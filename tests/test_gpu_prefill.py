@@ -150,6 +150,31 @@ def test_shapes_and_flags(G, orc, dtype, dk, dv, tiled, l2, scale):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("chunk,dk,dv,tiled,lens", [
+    (64, 128, 128, False, [1100, 0, 1, 700, 2050, 513]),
+    (32, 128, 128, True, [1100, 0, 1, 700, 2050, 513]),
+    (64, 64, 128, False, [1100, 0, 1, 700, 2050, 513]),
+    (32, 128, 64, False, [1100, 0, 1, 700, 2050, 513]),
+    (64, 64, 64, True, [1100, 0, 1, 700, 2050, 513]),
+    (64, 128, 128, False, [1100, 1100]),       # dense, three segments per sequence
+    (32, 128, 128, False, [1537, 1537, 1537]),  # dense, ragged last chunk and segment
+])
+def test_multi_segment_bf16(G, orc, chunk, dk, dv, tiled, lens):
+    """bf16 sequences long enough that the carry runs in several segments
+    (segment starts chained across segments), with empty, one-token and
+    ragged sequences in the same batch and nonzero initial states."""
+    sh = synth.LayerShape(2, 4, dk, dv)
+    inp = synth.make_prefill(31 + chunk + dk + dv, sh, lens, "bf16", state0_std=0.05, chunk_size=chunk,
+                             name="multiseg")
+    note(f"prefill multi-segment chunk={chunk} dk={dk} dv={dv} tiled={tiled} lens={lens}")
+    y = conv_inputs(orc, inp)
+    o, S = _run_gpu(G, inp, y, state0=inp.state0, heads_tiled=tiled)
+    o_ref, S_ref = _oracle(orc, inp, y, heads_tiled=tiled)
+    eo, es = _compare(inp, o, S, o_ref, S_ref)
+    note(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_qwen35_4k_bf16(G, orc):
     """B=1, T=4096, 16/32 heads, d=128, bf16, chunk 64 -- the benchmark's
     launch configuration; oracle on a sample of v-heads (full sequence)."""
