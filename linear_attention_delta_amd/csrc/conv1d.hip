@@ -105,16 +105,24 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int t) {
   return lo;
 }
 
-template <class E, int W, int TOK, bool ACT>
+template <class E, int W, int TOK, int RUN, bool ACT>
 __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
   typedef typename E::store_t T;
   constexpr int V = Vec<E>::N;
-  const int cg = blockIdx.y * blockDim.x + threadIdx.x;  // channel group
+  constexpr int SPAN = TOK * RUN;  // tokens per thread
+  // One-dimensional grid of (token span, channel block) pairs.  Workgroups
+  // go to the 8 XCDs round-robin by id; each XCD is given one contiguous run
+  // of token spans of a channel block, so the W-1 halo rows a span reads
+  // were fetched into that XCD's L2 by its predecessor.
+  const int ntb = (a.total_tokens + SPAN - 1) / SPAN;
+  int L = blockIdx.x;
+  if ((gridDim.x & 7) == 0) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int cg = (L / ntb) * blockDim.x + threadIdx.x;  // channel group
   const int c0 = cg * V;
   if (c0 >= a.channels) return;
-  const int t_begin = blockIdx.x * TOK;
+  const int t_begin = (L % ntb) * SPAN;
   if (t_begin >= a.total_tokens) return;
-  const int t_end = min(t_begin + TOK, a.total_tokens);
+  const int t_end = min(t_begin + SPAN, a.total_tokens);
 
   float w[V][W];
   float bias[V];
@@ -139,29 +147,46 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
     seq_end = a.cu_seqlens[seq + 1];
   }
 
-  // Fast path: the block and its W-1 token halo lie inside one sequence.
-  // Issue all TOK + W - 1 row loads at once, then walk the tokens with the
-  // last W inputs converted to fp32 in a sliding register window.
-  if (t_end - t_begin == TOK && t_begin - (W - 1) >= seq_start && t_end <= seq_end) {
-    typename Vec<E>::raw_t raw[TOK + W - 1];
+  // Fast path: the span and its W-1 token halo lie inside one sequence.  The
+  // span is walked in RUN blocks of TOK rows; the rows of block r + 1 are in
+  // flight while block r is computed, and the last W inputs stay converted
+  // to fp32 in a sliding register window, so no row is read twice.
+  if (t_end - t_begin == SPAN && t_begin - (W - 1) >= seq_start && t_end <= seq_end) {
+    typedef typename Vec<E>::raw_t raw_t;
+    raw_t halo[W - 1], cur[TOK];
 #pragma unroll
-    for (int j = 0; j < TOK + W - 1; j++)
-      raw[j] = Vec<E>::load_raw(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0);
-    float win[W][V];
+    for (int j = 0; j < W - 1; j++) halo[j] = Vec<E>::load_raw(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0);
 #pragma unroll
-    for (int j = 0; j < W - 1; j++) Vec<E>::cvt(raw[j], win[j]);
+    for (int j = 0; j < TOK; j++) cur[j] = Vec<E>::load_raw(x + (long)(t_begin + j) * a.stride_x + c0);
+    float wv[W][V];
 #pragma unroll
-    for (int tt = 0; tt < TOK; tt++) {
-      Vec<E>::cvt(raw[tt + W - 1], win[(tt + W - 1) % W]);
-      float out[V];
+    for (int j = 0; j < W - 1; j++) Vec<E>::cvt(halo[j], wv[j]);
 #pragma unroll
-      for (int i = 0; i < V; i++) {
-        float acc = bias[i];
+    for (int r = 0; r < RUN; r++) {
+      raw_t nxt[TOK];
+      if (r + 1 < RUN) {
 #pragma unroll
-        for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], win[(tt + j) % W][i], acc);
-        out[i] = ACT ? silu<E>(acc) : acc;
+        for (int j = 0; j < TOK; j++)
+          nxt[j] = Vec<E>::load_raw(x + (long)(t_begin + (r + 1) * TOK + j) * a.stride_x + c0);
       }
-      Vec<E>::store(y + (long)(t_begin + tt) * a.stride_y + c0, out);
+#pragma unroll
+      for (int tt = 0; tt < TOK; tt++) {
+        const int p = r * TOK + tt;  // wv[(p + j) % W] holds input p - (W-1) + j
+        Vec<E>::cvt(cur[tt], wv[(p + W - 1) % W]);
+        float out[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+          float acc = bias[i];
+#pragma unroll
+          for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], wv[(p + j) % W][i], acc);
+          out[i] = ACT ? silu<E>(acc) : acc;
+        }
+        Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
+      }
+      if (r + 1 < RUN) {
+#pragma unroll
+        for (int j = 0; j < TOK; j++) cur[j] = nxt[j];
+      }
     }
     return;
   }
@@ -294,7 +319,8 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
   }
 }
 
-constexpr int kConvTok = 8;
+constexpr int kConvTok = 8;  // rows per block
+constexpr int kConvRun = 1;  // blocks per thread (longer runs leave the SiLU arithmetic unhidden)
 
 template <class E, int W>
 hipError_t launch_w(const ConvArgs& a, hipStream_t s) {
@@ -307,11 +333,14 @@ hipError_t launch_w(const ConvArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.total_tokens > 0) {
-    dim3 grid((a.total_tokens + kConvTok - 1) / kConvTok, (groups + 255) / 256);
+    constexpr int span = kConvTok * kConvRun;
+    const long nblk = (long)((a.total_tokens + span - 1) / span) * ((groups + 255) / 256);
+    if (nblk > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)nblk);
     if (a.activation)
-      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, kConvRun, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_conv1d<E, W, kConvTok, kConvRun, false>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -754,348 +754,6 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   }
 }
 
-// ------------------------------------------------- phase 2, bf16 fast path
-//
-// One workgroup per (sequence, v-head, 16 columns of d_v), eight waves with
-// fixed roles and one barrier per chunk:
-//   wave 0  the state chain of chunk i:  X = K S -> R = V - a X -> U = Tt R
-//           -> S <- gl S + K^T (c U)
-//   wave 1  the output of chunk i-1:     O^T = b (S^T Q^T) + U^T P^T
-//   waves 2..7  stage chunk i+1's K, Tt, V and scalars and chunk i's Q, P
-//           into LDS, then issue the global loads of the next ones (the
-//           loads have a whole chunk period to land)
-// Wave 0 keeps its d_k x 16 fp32 state slice in MFMA accumulator form for the
-// whole sequence.  An accumulator tile (lane (c, g) holds rows 4g..4g+3 of
-// column c) is fed straight back as the next product's operand by letting
-// the K index of one 16x16x32 step run over rows {32m + 4g + e, 32m + 16 +
-// 4g + e} of two stacked tiles.  The other operand then needs, per lane, the
-// matching 8 elements of a row; the LDS copies of K, Q, Tt and P store each
-// 32-column block in that order (logical column 4g+e at 8g+e, 16+4g+e at
-// 8g+4+e), so the fragment is one 16-byte read.  K^T and V^T fragments come
-// from the row-major copies through the gfx950 transposing LDS read.
-// Wave 1 receives S (before the chunk's update) and U through small per-lane
-// handoff buffers.
-
-template <int C, int DK>
-struct alignas(16) ScanSmemBF {
-  static constexpr int KLD = DK + 16;  // row stride = 8 banks mod 64: conflict-free 16-byte fragment reads
-  static constexpr int CLD = C + 8;
-  static constexpr int NRT = C / 16;   // token tiles
-  static constexpr int NDT = DK / 16;  // state row tiles
-  uint16_t k[2][C][KLD];               // chain wave, chunk i (slot i & 1)
-  uint16_t tt[2][C][CLD];
-  uint16_t v[2][C][16];
-  uint16_t q[2][C][KLD];               // output wave, chunk i - 1
-  uint16_t p[2][C][CLD];
-  float sc[3][4][C];                   // a, b, c, e^{gamma_last}; slot i % 3
-  uint32_t hs[2][64][NDT * 2 + 4];     // S handoff: per lane NDT tiles x 4 bf16
-  uint32_t hu[2][64][NRT * 2 + 4];     // U handoff: per lane NRT tiles x 4 bf16
-};
-
-
-template <int C, int DK>
-__global__ void __launch_bounds__(512) k_scan_bf16(ScanArgs a) {
-  typedef ScanSmemBF<C, DK> SM;
-  constexpr int NRT = SM::NRT, NDT = SM::NDT;
-  constexpr int KS = DK / 32;          // 32-wide k steps over d_k
-  constexpr int PS = C / 32;           // 32-wide k steps over the chunk's tokens
-  static_assert(C % 32 == 0 && DK % 32 == 0, "chunk and d_k must be multiples of 32");
-  __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, g = lane >> 4, r4 = 4 * g;
-
-  // ---- (sequence, v-head, 16-column tile), XCD-aware: the tiles of one q/k
-  // head group share an XCD (and its L2) for K, Q, Tt and P
-  const int nblk = a.dv / 16;
-  const int G = a.hv / a.hk;
-  const int GS = G * nblk;
-  const int ngroups = a.num_seqs * a.hk;
-  const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
-  const int grp = (m8 / GS) * 8 + xcd;
-  if (grp >= ngroups) return;
-  const int local = m8 % GS;
-  const int seq = grp / a.hk, hk = grp % a.hk;
-  const int vh = local / nblk;
-  const int h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
-  const int dv0 = (local % nblk) * 16;
-  int s0, s1, cbase;
-  if (a.seqlen > 0) {
-    s0 = seq * a.seqlen;
-    s1 = s0 + a.seqlen;
-    cbase = seq * ((a.seqlen + C - 1) / C);
-  } else {
-    s0 = a.cu_seqlens[seq];
-    s1 = a.cu_seqlens[seq + 1];
-    cbase = a.chunk_offsets[seq];
-  }
-  const int nchunks = (s1 - s0 + C - 1) / C;
-  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
-  const uint16_t* mp = reinterpret_cast<const uint16_t*>(a.tinv);
-
-  // ---- staging (waves 2..7, three pairs): pair 0 moves K, pair 1 Q,
-  // pair 2 Tt, P, the V slice and the row scalars.  Chain-side inputs (K,
-  // Tt, V, scalars) of chunk i+1 and output-side inputs (Q, P) of chunk i are
-  // written to LDS in iteration i, then the next ones are loaded; six waves
-  // keep enough 16-byte loads in flight to draw near the per-CU L2 rate.
-  // Per-lane byte offsets are computed once; per chunk only the wave-uniform
-  // base pointers move.
-  const int sl = tid & 127;                  // lane within the staging pair
-  const int pair = (wave - 2) >> 1;          // 0: K, 1: Q, 2: Tt, P, V, scalars
-  constexpr int NKV = C * DK / 8 / 128;      // 16-byte vectors of K (or Q) per lane
-  constexpr int NMV = C * C / 8 / 128;       // of Tt (or P)
-  static_assert(NKV * 128 * 8 == C * DK && NMV * 128 * 8 == C * C && 2 * C <= 128, "staging");
-  const bool vlane = sl < 2 * C;             // V slice: 2 lanes per token row
-  u32x4 rx[NKV], rt[NMV], rp[NMV], rv, rs;
-  unsigned xgo[NKV];
-  const unsigned krow = (unsigned)a.stride_k * 2u, qrow = (unsigned)a.stride_q * 2u, vrow = (unsigned)a.stride_v * 2u;
-  const unsigned xrow = pair == 0 ? krow : qrow;
-#pragma unroll
-  for (int j = 0; j < NKV; j++) {
-    const int idx = sl + 128 * j, r = idx / (DK / 8), cv = idx % (DK / 8);
-    xgo[j] = (unsigned)r * xrow + 16u * cv;
-  }
-  const unsigned vgo = (unsigned)(sl >> 1) * vrow + 16u * (sl & 1);
-  const char* xbase = pair == 0 ? reinterpret_cast<const char*>(kp + (long)s0 * a.stride_k + (long)hk * DK)
-                                : reinterpret_cast<const char*>(qp + (long)s0 * a.stride_q + (long)hk * DK);
-  const char* vbase = reinterpret_cast<const char*>(vp + (long)s0 * a.stride_v + (long)h * a.dv + dv0);
-  const char* mbase = reinterpret_cast<const char*>(mp + ((long)cbase * a.hv + h) * (2 * C * C));
-  const char* sbase = reinterpret_cast<const char*>(a.scal + ((long)cbase * a.hv + h) * (4 * C));
-  const long mstep = (long)a.hv * (2 * C * C) * 2, sstep = (long)a.hv * (4 * C) * 4;
-  uint16_t (*const xlds)[C][SM::KLD] = pair == 0 ? sm.k : sm.q;
-
-  // pairs 0, 1: K (or Q) rows of chunk ch; rows past the end read as zero
-  auto load_x = [&](int ch) {
-    const int clen = min(C, s1 - (s0 + ch * C));
-    const char* xc = xbase + (long)ch * C * xrow;
-    if (clen == C) {
-#pragma unroll
-      for (int j = 0; j < NKV; j++) rx[j] = *reinterpret_cast<const u32x4*>(xc + xgo[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NKV; j++) {
-        const int r = (sl + 128 * j) / (DK / 8);
-        rx[j] = r < clen ? *reinterpret_cast<const u32x4*>(xc + xgo[j]) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_x = [&](int slot) {
-#pragma unroll
-    for (int j = 0; j < NKV; j++) {
-      const int idx = sl + 128 * j, r = idx / (DK / 8), lo = perm_lo(idx % (DK / 8));
-      *reinterpret_cast<u32x2*>(&xlds[slot][r][lo]) = u32x2{rx[j][0], rx[j][1]};
-      *reinterpret_cast<u32x2*>(&xlds[slot][r][lo + 8]) = u32x2{rx[j][2], rx[j][3]};
-    }
-  };
-  // pair 2: chain-side Tt, V slice, scalars of chunk ch
-  auto load_m = [&](int ch) {
-    const int clen = min(C, s1 - (s0 + ch * C));
-    const char* mc = mbase + ch * mstep;
-#pragma unroll
-    for (int j = 0; j < NMV; j++) rt[j] = *reinterpret_cast<const u32x4*>(mc + 16 * (sl + 128 * j));
-    if (vlane)
-      rv = (sl >> 1) < clen ? *reinterpret_cast<const u32x4*>(vbase + (long)ch * C * vrow + vgo)
-                            : u32x4{0u, 0u, 0u, 0u};
-    if (sl < C) rs = *reinterpret_cast<const u32x4*>(sbase + ch * sstep + 16 * sl);
-  };
-  auto store_m = [&](int slot, int slot3) {
-#pragma unroll
-    for (int j = 0; j < NMV; j++) {
-      const int idx = sl + 128 * j, r = idx / (C / 8), lo = perm_lo(idx % (C / 8));
-      *reinterpret_cast<u32x2*>(&sm.tt[slot][r][lo]) = u32x2{rt[j][0], rt[j][1]};
-      *reinterpret_cast<u32x2*>(&sm.tt[slot][r][lo + 8]) = u32x2{rt[j][2], rt[j][3]};
-    }
-    if (vlane) *reinterpret_cast<u32x4*>(&sm.v[slot][sl >> 1][8 * (sl & 1)]) = rv;
-    if (sl < C) *reinterpret_cast<u32x4*>(&sm.sc[slot3][0][0] + 4 * sl) = rs;
-  };
-  // pair 2: output-side P of chunk ch
-  auto load_p = [&](int ch) {
-    const char* pc = mbase + ch * mstep + C * C * 2;
-#pragma unroll
-    for (int j = 0; j < NMV; j++) rp[j] = *reinterpret_cast<const u32x4*>(pc + 16 * (sl + 128 * j));
-  };
-  auto store_p = [&](int slot) {
-#pragma unroll
-    for (int j = 0; j < NMV; j++) {
-      const int idx = sl + 128 * j, r = idx / (C / 8), lo = perm_lo(idx % (C / 8));
-      *reinterpret_cast<u32x2*>(&sm.p[slot][r][lo]) = u32x2{rp[j][0], rp[j][1]};
-      *reinterpret_cast<u32x2*>(&sm.p[slot][r][lo + 8]) = u32x2{rp[j][2], rp[j][3]};
-    }
-  };
-
-  // ---- wave 0: state slice in accumulator form; lane (c16, g) holds
-  // S[16u + 4g + e][dv0 + c16]
-  f32x4 S[NDT];
-  if (wave == 0) {
-    const float* sin = a.state_in ? a.state_in + ((long)seq * a.hv + h) * DK * a.dv : nullptr;
-#pragma unroll
-    for (int u = 0; u < NDT; u++)
-#pragma unroll
-      for (int e = 0; e < 4; e++) S[u][e] = sin ? sin[(long)(16 * u + r4 + e) * a.dv + dv0 + c16] : 0.f;
-  }
-  if (wave >= 2 && nchunks > 0) {
-    if (pair == 0) {
-      load_x(0);
-      store_x(0);
-      if (nchunks > 1) load_x(1);
-    } else if (pair == 1) {
-      load_x(0);
-    } else {
-      load_m(0);
-      store_m(0, 0);
-      if (nchunks > 1) load_m(1);
-      load_p(0);
-    }
-  }
-  uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)s0 * a.hv * a.dv + (long)h * a.dv + dv0 + r4;
-  const unsigned orow = (unsigned)(a.hv * a.dv);  // elements between tokens of o
-
-  // Iteration i (i = 0..nchunks) starts at a barrier: the chain wave works on
-  // chunk i, the output wave on chunk i - 1, the staging waves fill the slots
-  // the other two freed at this barrier.
-  if (wave == 0) {
-    for (int i = 0; i <= nchunks; i++) {
-      __syncthreads();
-      if (i == nchunks) break;
-      const int b = i & 1, b3 = i % 3;
-      bf16x8 bs[KS];
-#pragma unroll
-      for (int m = 0; m < KS; m++) {
-        const u32x2 lo = pack4_bf16(S[2 * m]), hi = pack4_bf16(S[2 * m + 1]);
-        bs[m] = frag2(lo, hi);
-        *reinterpret_cast<u32x4*>(&sm.hs[b][lane][4 * m]) = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-      // X = K S: token tiles t, k steps m over d_k
-      bf16x8 ak[KS][NRT];
-#pragma unroll
-      for (int m = 0; m < KS; m++)
-#pragma unroll
-        for (int t = 0; t < NRT; t++) ak[m][t] = ld_frag(&sm.k[b][16 * t + c16][32 * m + 8 * g]);
-      bf16x8 at[PS][NRT];
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++)
-#pragma unroll
-        for (int rt2 = 2 * pp; rt2 < NRT; rt2++) at[pp][rt2] = ld_frag(&sm.tt[b][16 * rt2 + c16][32 * pp + 8 * g]);
-      u32x2 vr[NRT];
-#pragma unroll
-      for (int t = 0; t < NRT; t++) vr[t] = ld_tr(&sm.v[b][16 * t + r4 + (c16 >> 2)][4 * (c16 & 3)]);
-      f32x4 X[NRT];
-#pragma unroll
-      for (int t = 0; t < NRT; t++) X[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < KS; m++)
-#pragma unroll
-        for (int t = 0; t < NRT; t++) X[t] = mfma16(ak[m][t], bs[m], X[t]);
-      // R = V - diag(a) X, in the same layout (lane: 4 tokens of column c16)
-      f32x4 R[NRT];
-#pragma unroll
-      for (int t = 0; t < NRT; t++) R[t] = bf4_to_f32(vr[t]) - ld4(&sm.sc[b3][0][16 * t + r4]) * X[t];
-      // U = Tt R: row tiles rt2, k steps pp over token tile pairs (2pp, 2pp+1)
-      f32x4 U[NRT];
-#pragma unroll
-      for (int t = 0; t < NRT; t++) U[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++) {
-        const bf16x8 br = frag2(pack4_bf16(R[2 * pp]), pack4_bf16(R[2 * pp + 1]));
-#pragma unroll
-        for (int rt2 = 2 * pp; rt2 < NRT; rt2++) U[rt2] = mfma16(at[pp][rt2], br, U[rt2]);
-      }
-      // K^T fragments: state tile u, token pair pp; lane (c16, g) gets
-      // K[32pp + 4g + e][16u + c16] and K[32pp + 16 + 4g + e][16u + c16]
-      bf16x8 akt[PS][NDT];
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++)
-#pragma unroll
-        for (int u = 0; u < NDT; u++) {
-          const uint16_t* p0 = &sm.k[b][32 * pp + r4 + (c16 >> 2)][32 * (u >> 1) + 8 * (c16 & 3) + 4 * (u & 1)];
-          akt[pp][u] = frag2(ld_tr(p0), ld_tr(p0 + 16 * SM::KLD));
-        }
-#pragma unroll
-      for (int t = 0; t < NRT; t++) {
-        *reinterpret_cast<u32x2*>(&sm.hu[b][lane][2 * t]) = pack4_bf16(U[t]);
-        U[t] = ld4(&sm.sc[b3][2][16 * t + r4]) * U[t];  // U2 = diag(c) U
-      }
-      const float gl = sm.sc[b3][3][0];
-      // S <- e^{gamma_last} S + K^T U2
-#pragma unroll
-      for (int u = 0; u < NDT; u++) S[u] = S[u] * gl;
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++) {
-        const bf16x8 bu = frag2(pack4_bf16(U[2 * pp]), pack4_bf16(U[2 * pp + 1]));
-#pragma unroll
-        for (int u = 0; u < NDT; u++) S[u] = mfma16(akt[pp][u], bu, S[u]);
-      }
-    }
-    if (a.state_out) {
-      float* so = a.state_out + ((long)seq * a.hv + h) * DK * a.dv;
-#pragma unroll
-      for (int u = 0; u < NDT; u++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) so[(long)(16 * u + r4 + e) * a.dv + dv0 + c16] = S[u][e];
-    }
-  } else if (wave == 1) {
-    for (int i = 0; i <= nchunks; i++) {
-      __syncthreads();
-      if (i == 0) continue;
-      const int j = i - 1, b = j & 1, b3 = j % 3;
-      const int clen = min(C, s1 - (s0 + j * C));
-      // Y^T = S^T Q^T: lane (c16, g) -> Y^T[4g + e][16t + c16]
-      bf16x8 aq[KS][NRT];
-#pragma unroll
-      for (int m = 0; m < KS; m++)
-#pragma unroll
-        for (int t = 0; t < NRT; t++) aq[m][t] = ld_frag(&sm.q[b][16 * t + c16][32 * m + 8 * g]);
-      bf16x8 ap[PS][NRT];
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++)
-#pragma unroll
-        for (int t = 2 * pp; t < NRT; t++) ap[pp][t] = ld_frag(&sm.p[b][16 * t + c16][32 * pp + 8 * g]);
-      f32x4 Y[NRT];
-#pragma unroll
-      for (int t = 0; t < NRT; t++) Y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < KS; m++) {
-        const bf16x8 as = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.hs[b][lane][4 * m]));
-#pragma unroll
-        for (int t = 0; t < NRT; t++) Y[t] = mfma16(as, aq[m][t], Y[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < NRT; t++) Y[t] = sm.sc[b3][1][16 * t + c16] * Y[t];
-      // + U^T P^T, then store O
-#pragma unroll
-      for (int pp = 0; pp < PS; pp++) {
-        const bf16x8 au = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.hu[b][lane][4 * pp]));
-#pragma unroll
-        for (int t = 2 * pp; t < NRT; t++) Y[t] = mfma16(au, ap[pp][t], Y[t]);
-      }
-      uint16_t* oc = obase + (long)j * C * orow;
-#pragma unroll
-      for (int t = 0; t < NRT; t++) {
-        const int r = 16 * t + c16;
-        if (r < clen) *reinterpret_cast<u32x2*>(oc + (unsigned)r * orow) = pack4_bf16(Y[t]);
-      }
-    }
-  } else {
-    for (int i = 0; i <= nchunks; i++) {
-      __syncthreads();
-      // registers hold chunk i+1's chain-side and chunk i's output-side inputs
-      if (pair == 0) {
-        if (i + 1 < nchunks) store_x((i + 1) & 1);
-        if (i + 2 < nchunks) load_x(i + 2);
-      } else if (pair == 1) {
-        if (i < nchunks) store_x(i & 1);
-        if (i + 1 < nchunks) load_x(i + 1);
-      } else {
-        if (i + 1 < nchunks) store_m((i + 1) & 1, (i + 1) % 3);
-        if (i < nchunks) store_p(i & 1);
-        if (i + 2 < nchunks) load_m(i + 2);
-        if (i + 1 < nchunks) load_p(i + 1);
-      }
-    }
-  }
-}
-
 template <class E, int C, int DK>
 hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
   const int G = a.hv / a.hk;
@@ -1112,16 +770,10 @@ hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
 template <class E, int C, int DK>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   constexpr bool BF = std::is_same<E, BF16>::value;
-  if constexpr (BF && C % 32 == 0) {
-    // bf16 fast path: one 16-column tile per workgroup, role-split waves
-    const int GS = (a.hv / a.hk) * (a.dv / 16);
-    const int per_xcd = (a.num_seqs * a.hk + 7) / 8;
-    hipLaunchKernelGGL((k_scan_bf16<C, DK>), dim3(8 * per_xcd * GS), dim3(512), 0, s, a);
-    return hipGetLastError();
-  }
-  // general path: bf16 chunk 16 with two 16-column tiles per workgroup (8
-  // waves), LDS double-buffered; fp32 with one tile (4 waves), single-buffered
-  // (the fp32 tiles fill the LDS)
+  // Sequential carry for what the segment-parallel path does not take:
+  // bf16 chunk 16 with two 16-column tiles per workgroup (8 waves), LDS
+  // double-buffered; fp32 with one tile (4 waves), single-buffered (the fp32
+  // tiles fill the LDS)
   constexpr int NT = BF ? 2 : 1;
   const int GS = (a.hv / a.hk) * (a.dv / (16 * NT));
   const int ngroups = a.num_seqs * a.hk;
