@@ -52,20 +52,25 @@ def prefill_alg_flops(T, hv, dk, dv, C=64):
     return per_chunk * (T / C) * hv
 
 
-def conv_alg_bytes(T, C, esize=2, W=4):
-    return T * C * esize * 2 + C * W * 4
+def conv_prepare_alg_bytes(T, C, hv, esize=2, W=4):
+    """Raw rows in, conv output (q | k | v) out, taps, and g, beta."""
+    return T * C * esize * 2 + C * W * 4 + 2 * T * hv * 4
 
 
 def decode_alg_bytes(B, hk, hv, dk, dv, esize=2):
     return 2 * B * hv * dk * dv * 4 + B * (2 * hk * dk + 2 * hv * dv) * esize + 2 * B * hv * 4
 
 
-KERNEL_SOURCES = {"conv1d": ["conv1d.hip"], "prefill_prepare": ["prefill.hip"],
-                  "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip"]}
+KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
+                  "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip"],
+                  "conv_step": ["conv1d.hip", "conv_math.h"]}
 # The GPU kernels each library call launches on the 4096-token bf16 layer
-# (the scan call runs the segment-parallel carry: two passes and a combine).
-CALL_KERNELS = {"conv1d": ["k_conv1d"], "prefill_prepare": ["k_prepare"],
-                "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"]}
+# (conv_prepare: the convolution, then the chunk prepare; the scan call runs
+# the segment-parallel carry: two passes and a combine) and on the
+# 64-sequence decode step.
+CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
+                "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
+                "conv_step": ["k_conv_step"]}
 
 
 def source_digest(kernel=None):
@@ -155,36 +160,30 @@ def main():
     for i in range(nsets):
         x = torch.from_numpy(inp.x).to(torch.bfloat16).to(dev)
         y = torch.empty((T, CC), dtype=torch.bfloat16, device=dev)
-        q = y[:, :a].view(T, sh.num_qk_heads, sh.head_dim_k)
-        k = y[:, a:2 * a].view(T, sh.num_qk_heads, sh.head_dim_k)
-        v = y[:, 2 * a:].view(T, sh.num_v_heads, sh.head_dim_v)
         g = torch.from_numpy(inp.g).to(dev)
         beta = torch.from_numpy(inp.beta).to(dev)
         o = torch.empty((T, sh.num_v_heads, sh.head_dim_v), dtype=torch.bfloat16, device=dev)
         st = torch.empty((1, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v), dtype=torch.float32, device=dev)
-        p = gdn.Prefill(q, k, v, seqlen=T, chunk_size=64)
-        sets.append(dict(x=x, y=y, q=q, k=k, v=v, g=g, beta=beta, o=o, st=st, p=p))
+        sets.append(dict(x=x, y=y, g=g, beta=beta, o=o, st=st))
+    # one bound problem (dims + workspace) serves every buffer set
+    cp = gdn.ConvPrefill(sets[0]["x"], w, num_qk_heads=sh.num_qk_heads, num_v_heads=sh.num_v_heads,
+                         head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, seqlen=T, chunk_size=64)
     torch.cuda.synchronize()
-
-    conv_p = gdn.Conv1d(sets[0]["x"], w, seqlen=T)
 
     def step(s, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        conv_p(s["x"], s["y"])
+        cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"])
         if ev is not None:
             ev[1].record(stream)
-        s["p"].prepare(s["q"], s["k"], s["g"], s["beta"])
+        cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"])
         if ev is not None:
             ev[2].record(stream)
-        s["p"].scan(s["q"], s["k"], s["v"], s["g"], s["beta"], s["o"], None, s["st"])
-        if ev is not None:
-            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -196,40 +195,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
-    k_conv = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3   # us
-    k_prep = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    k_scan = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    k_cp = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3   # us
+    k_scan = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = T / (ms_per_step * 1e-3)
 
     # warm figure: one buffer set, back to back (MALL may serve it)
-    warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(50)]
+    warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
     for i in range(10):
         step(sets[0])
     for i in range(50):
         step(sets[0], warm_evs[i])
     torch.cuda.synchronize()
-    warm_scan = float(np.mean([e[2].elapsed_time(e[3]) for e in warm_evs]) * 1e3)
-    warm_prep = float(np.mean([e[1].elapsed_time(e[2]) for e in warm_evs]) * 1e3)
-    warm_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in warm_evs]) * 1e3)
+    warm_cp = float(np.mean([e[0].elapsed_time(e[1]) for e in warm_evs]) * 1e3)
+    warm_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in warm_evs]) * 1e3)
 
     B_pre = prefill_alg_bytes(T, sh.num_qk_heads, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
     F_pre = prefill_alg_flops(T, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
-    B_conv = conv_alg_bytes(T, CC)
-    kernels = {"conv1d": float(k_conv.mean()), "prefill_prepare": float(k_prep.mean()),
-               "prefill_scan": float(k_scan.mean())}
+    B_cp = conv_prepare_alg_bytes(T, CC, sh.num_v_heads)
+    kernels = {"conv_prepare": float(k_cp.mean()), "prefill_scan": float(k_scan.mean())}
     dominant = max(kernels, key=kernels.get)
     dom_us = kernels[dominant]
-    # the prefill kernels must together move the prefill's algorithmic bytes;
-    # the dominant kernel is charged with the bytes of the call it serves
-    dom_bytes = {"conv1d": B_conv, "prefill_prepare": B_pre, "prefill_scan": B_pre}[dominant]
+    dom_bytes = {"conv_prepare": B_cp, "prefill_scan": B_pre}[dominant]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = read_traffic(dominant, inp.name)
-    roofline = {"bound": "hbm", "kernel": dominant, "gpu_kernels": CALL_KERNELS[dominant], "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "alg_bytes_per_launch": int(dom_bytes),
+    roofline = {"bound": "hbm", "kernel": dominant, "gpu_kernels": CALL_KERNELS[dominant],
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "alg_bytes_per_launch": int(dom_bytes),
                 "avg_launch_us": round(dom_us, 2)}
-    pre_us = kernels["prefill_prepare"] + kernels["prefill_scan"]
+    step_us = kernels["conv_prepare"] + kernels["prefill_scan"]
 
     # ----------------------------------------------------------------- decode
     dinp = synth.decode_b64_bf16()
@@ -320,17 +314,17 @@ def main():
         "data": "synthetic (seeded; Qwen3.5-4B-shaped GDN layer)",
         "config": {"workload": inp.name, "global_batch": 1, "seq_len": T, "qk_heads": sh.num_qk_heads,
                    "v_heads": sh.num_v_heads, "head_dim": sh.head_dim_k, "chunk": 64, "conv_width": 4,
-                   "step": "conv1d+SiLU -> prefill prepare -> prefill scan", "buffer_sets": nsets},
+                   "step": "conv1d+SiLU -> prefill prepare -> prefill scan (two library calls)",
+                   "buffer_sets": nsets},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v, 2) for k, v in kernels.items()},
         "gpu_ms_per_step_events": round(gpu_ms / args.steps, 5),
-        "prefill_only": {"us": round(pre_us, 2), "tokens_per_s": round(T / (pre_us * 1e-6), 1),
-                         "hbm_frac": round(B_pre / (pre_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "mfma_frac_bf16": round(F_pre / (pre_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "step_kernels": {"us": round(step_us, 2), "tokens_per_s": round(T / (step_us * 1e-6), 1),
+                         "hbm_frac": round(B_pre / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_frac_bf16": round(F_pre / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "alg_bytes": int(B_pre), "alg_flops": int(F_pre)},
-        "warm_single_set_us": {"conv1d": round(warm_conv, 2), "prefill_prepare": round(warm_prep, 2),
-                               "prefill_scan": round(warm_scan, 2)},
+        "warm_single_set_us": {"conv_prepare": round(warm_cp, 2), "prefill_scan": round(warm_scan, 2)},
         "decode": decode,
         "source_digest": {k: source_digest(k) for k in KERNEL_SOURCES},
     }

@@ -195,6 +195,54 @@ gdn_status gdn_prefill_scan(const gdn_dims *d, const void *q, const void *k,
                             size_t ws_bytes, void *stream);
 
 /*
+ * Convolution and prefill phase 1 in one call: the layer's short causal
+ * conv1d + SiLU (Vallmo.jl README, "What's here") over the raw projected rows
+ * x, whose channels are ordered [q | k | v] (C_conv = 2 H_k d_k + H_v d_v),
+ * followed by gdn_prefill_prepare on the q and k it produced.  The result is
+ * exactly that of
+ *     gdn_conv1d(N, N_tok, seqlen, cu_seqlens, C_conv, conv_width, dtype, x,
+ *                stride_x, conv_weight, conv_bias, conv_state, 1, y, stride_y)
+ *     gdn_prefill_prepare(d, y, y + H_k d_k, g, beta, cu_seqlens, workspace)
+ * bit for bit (y, conv_state and the workspace); it is those two calls
+ * with one validation.  Afterwards gdn_prefill_scan(d, y, y + H_k d_k,
+ * y + 2 H_k d_k, ...) with the same workspace completes the prefill
+ * (gdn_prefill_conv_chunked does both).
+ *
+ * d: the problem; its stride_q, stride_k and stride_v must all equal
+ * stride_y (q, k, v are column blocks of y).  conv_width, x, stride_x,
+ * conv_weight, conv_bias, conv_state: as gdn_conv1d (conv_state is read and
+ * then advanced to the last conv_width-1 raw inputs of each sequence).
+ * y: [N_tok] rows of C_conv channels in dtype, token stride stride_y; it
+ * must not overlap x.  g, beta, cu_seqlens, workspace: as gdn_prefill_chunked.
+ * Errors as gdn_prefill_prepare and gdn_conv1d; nothing is queued on error.
+ */
+gdn_status gdn_prefill_conv_prepare(const gdn_dims *d, int32_t conv_width,
+                                    const void *x, int64_t stride_x,
+                                    const float *conv_weight,
+                                    const float *conv_bias, void *conv_state,
+                                    const float *g, const float *beta,
+                                    const int32_t *cu_seqlens, void *y,
+                                    int64_t stride_y, void *workspace,
+                                    size_t ws_bytes, void *stream);
+
+/*
+ * The whole prefill from raw rows: gdn_prefill_conv_prepare followed by
+ * gdn_prefill_scan on the q, k, v column blocks of y, on one stream.
+ * state_in, o, state_out: as gdn_prefill_chunked.  Both halves are
+ * validated before anything is queued.
+ */
+gdn_status gdn_prefill_conv_chunked(const gdn_dims *d, int32_t conv_width,
+                                    const void *x, int64_t stride_x,
+                                    const float *conv_weight,
+                                    const float *conv_bias, void *conv_state,
+                                    const float *g, const float *beta,
+                                    const float *state_in,
+                                    const int32_t *cu_seqlens, void *y,
+                                    int64_t stride_y, void *o, float *state_out,
+                                    void *workspace, size_t ws_bytes,
+                                    void *stream);
+
+/*
  * One decode step (the O(1) recurrent step of the oxydllm notes): one new
  * token for each of d->num_seqs sequences (d->seqlen must be 1 and
  * d->total_tokens == d->num_seqs; chunk_size is ignored).

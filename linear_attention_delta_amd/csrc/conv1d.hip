@@ -12,7 +12,7 @@
 // Bit-exact arithmetic: acc = bias (or 0); acc = fma(w_j, x_j, acc) for
 // j = 0..W-1; y = acc / (1 + exp_cw(-acc)); bf16 output rounded to nearest
 // even (NaN -> 0x7fc0).  For bf16 outputs the SiLU is evaluated on a fast
-// path that provably rounds to the same bf16 (silu_for_bf16 below), since
+// path that provably rounds to the same bf16 (silu_for_bf16 in conv_math.h), since
 // the exact exponential and division dominate the kernel's ALU time.
 // Contraction is switched off in this file so the compiler adds or removes
 // no fused multiply-adds.
@@ -20,6 +20,7 @@
 
 #include <type_traits>
 
+#include "conv_math.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -41,17 +42,8 @@ struct Vec<BF16> {
     }
   }
   __device__ __forceinline__ static void load(const uint16_t* p, float* out) { cvt(load_raw(p), out); }
-  // Round to nearest even with the hardware conversion; a NaN is first made
-  // the canonical quiet NaN so that it converts to 0x7fc0 like f32_to_bf16.
   __device__ __forceinline__ static void store(uint16_t* p, const float* v) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float lo = v[2 * i] != v[2 * i] ? __uint_as_float(0x7fc00000u) : v[2 * i];
-      const float hi = v[2 * i + 1] != v[2 * i + 1] ? __uint_as_float(0x7fc00000u) : v[2 * i + 1];
-      w[i] = cvt_bf16x2(lo, hi);
-    }
-    *reinterpret_cast<u32x4*>(p) = w;
+    *reinterpret_cast<u32x4*>(p) = conv_pack_bf16x8(v);
   }
 };
 template <>
@@ -69,31 +61,6 @@ struct Vec<F32> {
     *reinterpret_cast<f32x4*>(p) = w;
   }
 };
-
-__device__ __forceinline__ float silu_exact(float a) { return a / (1.0f + exp_cw(-a)); }
-
-// SiLU for an output that is rounded to bf16.  The fp32 value of
-// a * (1 + 2^(-a log2 e))^-1 from the hardware exponential and reciprocal is
-// within 9 ulp of silu_exact(a) for every fp32 a > -8 (checked over all 2^32
-// inputs on gfx950), so both round to the same bf16 unless a bf16 rounding
-// midpoint lies within that distance.  Results whose low 16 bits are within
-// 16 of the midpoint pattern 0x8000, and every a <= -8 (where the relative
-// error of the exponential grows with |a|), take the exact path instead:
-// the rounded output is that of silu_exact, bit for bit, at a fraction of
-// its cost.  NaN stays NaN on both paths (the store canonicalises it).
-__device__ __forceinline__ float silu_for_bf16(float a) {
-  const float e = __builtin_amdgcn_exp2f(-a * 1.44269504088896341f);
-  const float q = a * __builtin_amdgcn_rcpf(1.0f + e);
-  const uint32_t low = __float_as_uint(q) & 0xffffu;
-  if (!(a > -8.0f) || low - (0x8000u - 16u) <= 32u) return silu_exact(a);
-  return q;
-}
-
-template <class E>
-__device__ __forceinline__ float silu(float a) {
-  if constexpr (std::is_same<E, BF16>::value) return silu_for_bf16(a);
-  return silu_exact(a);
-}
 
 // Sequence containing token t: the last s with cu[s] <= t.
 __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int t) {
@@ -176,11 +143,13 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
         float out[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-          float acc = bias[i];
+          float xv[W];
 #pragma unroll
-          for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], wv[(p + j) % W][i], acc);
-          out[i] = ACT ? silu<E>(acc) : acc;
+          for (int j = 0; j < W; j++) xv[j] = wv[(p + j) % W][i];
+          if constexpr (ACT && std::is_same<E, BF16>::value) out[i] = conv_sum<W>(bias[i], w[i], xv);
+          else out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
         }
+        if constexpr (ACT && std::is_same<E, BF16>::value) silu8_for_bf16(out);
         Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
       }
       if (r + 1 < RUN) {
@@ -228,10 +197,10 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
     float out[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
-      float acc = bias[i];
+      float xv[W];
 #pragma unroll
-      for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[i][j], hist[j][i], acc);
-      out[i] = ACT ? silu<E>(acc) : acc;
+      for (int j = 0; j < W; j++) xv[j] = hist[j][i];
+      out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
     }
     Vec<E>::store(y + (long)t * a.stride_y + c0, out);
 #pragma unroll
@@ -306,10 +275,14 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
   float out[V];
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    float acc = a.bias ? a.bias[c0 + i] : 0.0f;
+    const float bias = a.bias ? a.bias[c0 + i] : 0.0f;
+    float wj[W], xv[W];
 #pragma unroll
-    for (int j = 0; j < W; j++) acc = __builtin_fmaf(a.weight[(long)(c0 + i) * W + j], hist[j][i], acc);
-    out[i] = a.activation ? silu<E>(acc) : acc;
+    for (int j = 0; j < W; j++) {
+      wj[j] = a.weight[(long)(c0 + i) * W + j];
+      xv[j] = hist[j][i];
+    }
+    out[i] = a.activation ? conv_point<E, W, true>(bias, wj, xv) : conv_point<E, W, false>(bias, wj, xv);
   }
   Vec<E>::store(y + (long)seq * a.stride_y + c0, out);
   if (win) {

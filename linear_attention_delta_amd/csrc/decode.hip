@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(256) k_decode(ScanArgs a) {
   const int b = blockIdx.x / a.hv;
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
 
   const int slot = a.state_slots ? a.state_slots[b] : b;
   if (slot < 0 || slot >= a.num_slots) {  // bad slot: flag the output, leave every state alone
@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) k_decode(ScanArgs a) {
   float vv[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) vv[j] = load_elem<E>(a.v, (long)b * a.stride_v + (long)h * DV + 4 * cg + j);
-  __syncthreads();
+  lds_barrier();
   kk = part[0][0] + part[1][0] + part[2][0] + part[3][0];
   qq = part[0][1] + part[1][1] + part[2][1] + part[3][1];
   kq = part[0][2] + part[1][2] + part[2][2] + part[3][2];
@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(256) k_decode(ScanArgs a) {
   }
   red[rg][cg][0] = pk;
   red[rg][cg][1] = pq;
-  __syncthreads();
+  lds_barrier();
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < RG; r++) {

@@ -405,6 +405,106 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, 
   return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
 }
 
+gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+                                    const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
+                                    const float* beta, const int32_t* cu_seqlens, void* y, int64_t stride_y,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  const int64_t cc = 2LL * d->num_qk_heads * d->head_dim_k + (int64_t)d->num_v_heads * d->head_dim_v;
+  const int vec = d->dtype == GDN_BF16 ? 8 : 4;
+  if (conv_width < 2 || conv_width > 8) return fail(GDN_ERR_UNSUPPORTED, "conv_width must be in [2, 8] (got %d)", conv_width);
+  if (stride_x < cc || stride_y < cc || stride_x % vec || stride_y % vec)
+    return fail(GDN_ERR_INVALID_ARG, "stride_x and stride_y must be >= %lld channels and multiples of %d", (long long)cc, vec);
+  if (d->stride_q != stride_y || d->stride_k != stride_y || d->stride_v != stride_y)
+    return fail(GDN_ERR_INVALID_ARG, "q, k and v are the column blocks of y: d's strides must equal stride_y");
+  if (d->total_tokens > 0) {
+    if (!x || !y) return fail(GDN_ERR_INVALID_ARG, "x and y must be non-NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(GDN_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
+    const char* x0 = reinterpret_cast<const char*>(x);
+    const char* y0 = reinterpret_cast<const char*>(y);
+    const size_t xb = ((size_t)(d->total_tokens - 1) * stride_x + cc) * esz;
+    const size_t yb = ((size_t)(d->total_tokens - 1) * stride_y + cc) * esz;
+    if (x0 < y0 + yb && y0 < x0 + xb) return fail(GDN_ERR_INVALID_ARG, "x and y must not overlap");
+  }
+  if (!conv_weight || !aligned(conv_weight, 4))
+    return fail(GDN_ERR_INVALID_ARG, "conv_weight must be non-NULL and 4-byte aligned");
+  if (conv_bias && !aligned(conv_bias, 4)) return fail(GDN_ERR_INVALID_ARG, "conv_bias must be 4-byte aligned");
+  if (conv_state && !aligned(conv_state, 16)) return fail(GDN_ERR_INVALID_ARG, "conv_state must be 16-byte aligned");
+  const void* q = y;
+  const void* k = reinterpret_cast<const char*>(y) + (size_t)d->num_qk_heads * d->head_dim_k * (d->dtype == GDN_BF16 ? 2 : 4);
+  if ((st = check_scan_ptrs(d, q, k, nullptr, g, beta, cu_seqlens, false)) != GDN_OK) return st;
+  if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
+
+  gdn::ConvArgs ca;
+  ca.num_seqs = d->num_seqs;
+  ca.total_tokens = d->total_tokens;
+  ca.seqlen = d->seqlen;
+  ca.cu_seqlens = cu_seqlens;
+  ca.channels = (int)cc;
+  ca.width = conv_width;
+  ca.dtype = d->dtype;
+  ca.activation = 1;
+  ca.x = x;
+  ca.stride_x = stride_x;
+  ca.weight = conv_weight;
+  ca.bias = conv_bias;
+  ca.conv_state = conv_state;
+  ca.y = y;
+  ca.stride_y = stride_y;
+
+  gdn::ScanArgs a = make_args(d);
+  a.q = q;
+  a.k = k;
+  a.g = g;
+  a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  carve(a, d, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  // The two kernels back to back: folding the convolution into the prepare
+  // kernel was measured slower (both are bound by vector-instruction issue,
+  // and the stand-alone convolution overlaps its arithmetic with its memory
+  // traffic across many more waves).
+  if ((e = gdn::launch_conv1d(ca, s)) != hipSuccess) return hip_fail(e, "conv1d launch");
+  if ((st = run_prepare(a, s)) != GDN_OK) return st;
+  if (debug_enabled() && d->total_tokens > 0) {
+    st = debug_check(s, "conv y", y, (long)(d->total_tokens - 1) * stride_y + cc, d->dtype);
+    if (st != GDN_OK) return st;
+  }
+  return ok();
+}
+
+gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+                                    const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
+                                    const float* beta, const float* state_in, const int32_t* cu_seqlens, void* y,
+                                    int64_t stride_y, void* o, float* state_out, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  // validate the scan half before queuing anything
+  if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
+  if (state_in && state_out && state_in != state_out) {
+    const size_t sbytes = (size_t)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v * 4;
+    const char* a0 = reinterpret_cast<const char*>(state_in);
+    const char* b0 = reinterpret_cast<const char*>(state_out);
+    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
+      return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
+  }
+  if ((st = gdn_prefill_conv_prepare(d, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta,
+                                     cu_seqlens, y, stride_y, workspace, ws_bytes, stream)) != GDN_OK)
+    return st;
+  const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
+  const char* y0 = reinterpret_cast<const char*>(y);
+  const void* q = y0;
+  const void* k = y0 + (size_t)d->num_qk_heads * d->head_dim_k * esz;
+  const void* v = y0 + (size_t)2 * d->num_qk_heads * d->head_dim_k * esz;
+  return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
+}
+
 gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, int32_t num_slots, const int32_t* state_slots, void* o,
                            void* stream) {

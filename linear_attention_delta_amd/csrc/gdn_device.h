@@ -123,6 +123,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Index of the calling wave in its workgroup, as a value the compiler knows
+// to be uniform across the wave: index arithmetic and loops that depend on
+// it then run on the scalar unit instead of costing vector instructions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Workgroup barrier for LDS traffic: every wave's earlier LDS writes are
+// visible to every wave's later LDS reads.  Unlike __syncthreads(), whose
+// workgroup fence also covers global memory and so makes each wave wait
+// until all of its global loads have returned and its global stores have
+// been acknowledged, this orders LDS only: global stores keep draining and
+// prefetched loads stay in flight across the barrier.  For workgroups whose
+// waves exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Make this wave's earlier LDS writes visible to its later LDS reads
 // (other lanes of the same wave).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -29,6 +29,7 @@
 // Phase 2 (k_scan): one workgroup per (sequence, v-head, NT*16 columns of
 // d_v) walks the chunks in order with its d_k x NT*16 fp32 slice of S in
 // registers; per chunk only the four state-dependent products remain.
+#include <algorithm>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -169,6 +170,8 @@ struct alignas(16) PrepSmem {
   float gam[HPW][C], bet[HPW][C], rk[C], rq[C];
 };
 
+
+
 // X Y for 16x16 fp32 tiles given X^T and Y in the accumulator layout.
 __device__ __forceinline__ f32x4 mm_tt(f32x4 xt, f32x4 y) {
   f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -221,27 +224,31 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   constexpr int NTW = (NT + 3) / 4;            // per wave
   constexpr int L = SM::ALD;
   __shared__ SM sm;
-  int seq, start, len;
-  if (!chunk_of(a, C, blockIdx.x, seq, start, len)) return;
+  // one-dimensional grid: workgroup = (chunk, q/k head with HPW of its v-heads)
   const int G = a.hv / a.hk;
-  const int hk = blockIdx.y / (G / HPW);
-  const int vh0 = (blockIdx.y % (G / HPW)) * HPW;
+  const int ngroups = a.hv / HPW;
+  const long chunk = blockIdx.x / ngroups;
+  const int grp = blockIdx.x % ngroups;
+  int seq, start, len;
+  if (!chunk_of(a, C, (int)chunk, seq, start, len)) return;
+  const int hk = grp / (G / HPW);
+  const int vh0 = (grp % (G / HPW)) * HPW;
   int hs[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; j++) hs[j] = a.tiled ? (hk + (vh0 + j) * a.hk) : (hk * G + vh0 + j);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
-  // ---- stage K and Q rows (zero past the end of the sequence); all loads
-  // are issued before any is used.  Row norms come from the registers.
+  // ---- load K and Q rows (zero past the end of the sequence) and the
+  // gates; all loads are issued before any is used
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int VPR = DK / EPV;  // 16-byte vectors per row
+  constexpr int NV = 2 * C * VPR / 256;
+  static_assert(NV * 256 == 2 * C * VPR, "K/Q staging must tile the workgroup");
+  u32x4 w[NV];
   {
-    constexpr int EPV = 16 / sizeof(T);
-    constexpr int VPR = DK / EPV;  // 16-byte vectors per row
-    constexpr int NV = 2 * C * VPR / 256;
-    static_assert(NV * 256 == 2 * C * VPR, "K/Q staging must tile the workgroup");
     const T* kp = reinterpret_cast<const T*>(a.k);
     const T* qp = reinterpret_cast<const T*>(a.q);
-    u32x4 w[NV];
 #pragma unroll
     for (int j = 0; j < NV; j++) {
       const int idx = tid + 256 * j;
@@ -254,11 +261,15 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
         w[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
       }
     }
-    float gv = 0.f, bv = 0.f;
-    if (wave < HPW && lane < len) {
-      gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
-      bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
-    }
+  }
+  float gv = 0.f, bv = 0.f;
+  if (wave < HPW && lane < len) {
+    gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
+    bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
+  }
+
+  // ---- stage K and Q into LDS with the per-row inverse norms
+  {
 #pragma unroll
     for (int j = 0; j < NV; j++) {
       const int idx = tid + 256 * j;
@@ -279,15 +290,15 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
         if (which) sm.rq[r] = a.scale * inv; else sm.rk[r] = inv;
       }
     }
-    if (wave < HPW) {
-      const float gm = wave_prefix_sum(gv, lane);
-      if (lane < C) {
-        sm.gam[wave][lane] = gm;
-        sm.bet[wave][lane] = bv;
-      }
+  }
+  if (wave < HPW) {
+    const float gm = wave_prefix_sum(gv, lane);
+    if (lane < C) {
+      sm.gam[wave][lane] = gm;
+      sm.bet[wave][lane] = bv;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- transposed Gram tiles D[s][r] = k_s . x_r (x = k or q) of the lower
   // tile (i, j), j <= i: lane (c, g) holds r = 16i + c, s = 16j + 4g + e.
   //   P[r][s] = rq_r rk_s e^{gamma_r - gamma_s} q_r.k_s          (s <= r) -> workspace
@@ -324,7 +335,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
         const int s = s0 + e;
         v[e] = s <= r ? fr * sm.rk[s] * __expf(gr - sm.gam[hh][s]) * acc[e] : 0.f;
       }
-      T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C) + C * C;
+      T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C;
       if constexpr (std::is_same<E, BF16>::value) {
         *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
       } else {
@@ -339,7 +350,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
     const int r = 16 * i + c16, s0 = 16 * j + r4;
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
-      T* pout = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C) + C * C;
+      T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C;
       if constexpr (std::is_same<E, BF16>::value) {
         *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{0u, 0u};
       } else {
@@ -349,7 +360,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   }
   // ---- per-token scalars a, b, c and e^{gamma_last}
   if (wave < HPW && lane < C) {
-    float* scal = a.scal + ((long)blockIdx.x * a.hv + hs[wave]) * (4 * C);
+    float* scal = a.scal + (chunk * a.hv + hs[wave]) * (4 * C);
     const float gm = sm.gam[wave][lane], glast = sm.gam[wave][C - 1];
     const float eg = __expf(gm);
     scal[lane] = eg * sm.rk[lane];
@@ -357,7 +368,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
     scal[2 * C + lane] = __expf(glast - gm) * sm.rk[lane];
     scal[3 * C + lane] = lane == 0 ? __expf(glast) : 0.f;
   }
-  __syncthreads();  // K and Q are dead: A takes their place
+  lds_barrier();  // K and Q are dead: A takes their place
 #pragma unroll
   for (int n = 0; n < NTW; n++) {
     const int t = wave + 4 * n;
@@ -379,7 +390,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- diagonal 16x16 blocks, inverted in registers, written back in place
   for (int blk = wave; blk < HPW * NRT; blk += 4) {
     const int hh = blk / NRT, d = blk % NRT;
@@ -387,7 +398,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
     const f32x4 inv = inv16(A0, L, lane);
     st_c(A0, L, inv, lane);
   }
-  __syncthreads();
+  lds_barrier();
   // ---- merge 16 -> 32: [[X, 0], [Y, Z]]^{-1} has lower-left block -Z (Y X)
   if constexpr (C >= 32) {
     for (int m = wave; m < HPW * (NRT / 2); m += 4) {
@@ -397,7 +408,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       const f32x4 l = mm_tt(ld_ct(at + (b + 16) * L + b + 16, L, lane), w);
       st_c(at + (b + 16) * L + b, L, -l, lane);
     }
-    __syncthreads();
+    lds_barrier();
   }
   // ---- merge 32 -> 64: lower-left 32x32 block -Z (Y X), one 16-column
   // strip jc of it per wave; Y is still the original A there
@@ -422,17 +433,17 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       l2 = -mm_tt(ld_ct(blk(2, 2), L, lane), w2);
       l3 = -(mm_tt(ld_ct(blk(3, 2), L, lane), w2) + mm_tt(ld_ct(blk(3, 3), L, lane), w3));
     }
-    __syncthreads();  // every wave has read the original A blocks
+    lds_barrier();  // every wave has read the original A blocks
     if (act) {
       st_c(blk(2, jc), L, l2, lane);
       st_c(blk(3, jc), L, l3, lane);
     }
-    __syncthreads();
+    lds_barrier();
   }
   // ---- Tt = inv diag(beta), upper triangle zero, to the workspace
 #pragma unroll
   for (int hh = 0; hh < HPW; hh++) {
-    T* out = reinterpret_cast<T*>(a.tinv) + ((long)blockIdx.x * a.hv + hs[hh]) * (2 * C * C);
+    T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);
     for (int idx = tid; idx < C * C / 4; idx += 256) {
       const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0]);
@@ -540,7 +551,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   constexpr int STW = DK / 64;     // state row tiles per wave (per column tile)
   constexpr int KLD = SM::KLD, CLD = SM::CLD;
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tw = wave >> 2, lw = wave & 3;   // column tile, wave within it
   const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
@@ -579,7 +590,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   }
   const int nchunks = (s1 - s0 + C - 1) / C;
 
-  __syncthreads();  // zeroing done
+  lds_barrier();  // zeroing done
 
   // ---- initial state: wave (tw, lw) owns rows [lw*DK/4, (lw+1)*DK/4) of tile tw
   f32x4 S[STW];
@@ -685,7 +696,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     const int sb = ch & 1;                 // state operand buffer read this chunk
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
-    __syncthreads();                       // B0: staged chunk and S^T visible
+    lds_barrier();                       // B0: staged chunk and S^T visible
     if (ch + 1 < nchunks) load_chunk(ch + 1);
 
     // ---- X = K S, R = V - diag(a) X -> R^T
@@ -695,7 +706,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       const int s = 16 * lw + r4;
       st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
-    __syncthreads();                       // B1
+    lds_barrier();                       // B1
     // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
     if (lw < NRT) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -705,7 +716,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       st4(&sm.ut[tw][c16][s], U);
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
-    __syncthreads();                       // B2
+    lds_barrier();                       // B2
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT) {
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
@@ -736,7 +747,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     // ---- stage the next chunk (single-buffered: wait until all waves are
     // done with this chunk's staged data)
     if (ch + 1 < nchunks) {
-      if (!DB) __syncthreads();
+      if (!DB) lds_barrier();
       store_chunk(nb);
     }
   }
@@ -757,13 +768,11 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
 template <class E, int C, int DK>
 hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
   const int G = a.hv / a.hk;
-  if (G % 2 == 0) {
-    dim3 grid(a.max_chunks, a.hv / 2), block(256);
-    hipLaunchKernelGGL((k_prepare<E, C, DK, 2>), grid, block, 0, s, a);
-  } else {
-    dim3 grid(a.max_chunks, a.hv), block(256);
-    hipLaunchKernelGGL((k_prepare<E, C, DK, 1>), grid, block, 0, s, a);
-  }
+  const dim3 block(256);
+  const int hpw = G % 2 == 0 ? 2 : 1;
+  const dim3 grid((unsigned)((long)a.max_chunks * (a.hv / hpw)));  // one (chunk, head group) per workgroup
+  if (hpw == 2) hipLaunchKernelGGL((k_prepare<E, C, DK, 2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_prepare<E, C, DK, 1>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
   constexpr int SVT = DV / 16;                // tiles below SVT are state columns
   static_assert(NCT * 16 * NW == DV + DK, "columns must split over the waves");
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = 4 * (lane >> 4);
   int n, hk, h;
   block_unit(a, n, hk, h);
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
   if (nch > 1) st.load(ch0 + 1);
   u32x2 ob[NCT][C / 16];
   for (int i = 0; i < nch; i++) {
-    __syncthreads();
+    lds_barrier();
     const int b = i & 1;
     if (i + 1 < nch) st.store(sm, b ^ 1);
     if (i + 2 < nch) st.load(ch0 + i + 2);
@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
   constexpr int PLD = DK + 8;
   uint16_t* img = reinterpret_cast<uint16_t*>(&sm);
   static_assert(sizeof(SM) >= DK * PLD * 2, "transition image must fit the chunk buffers");
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int j = 0; j < NCT; j++) {
     const int gt = wave * NCT + j;
@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
         for (int e = 0; e < 4; e++) img[(16 * u + r4 + e) * PLD + 16 * (gt - SVT) + c16] = bf16_rne(Z[u][j][e]);
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint16_t* phi = a.seg_phi + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DK;
   for (int f = wave; f < NDT * (DK / 32); f += NW) {
     const int u = f / (DK / 32), m = f % (DK / 32);
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
   static_assert(PV * 256 * 8 == DK * DK && BV * 256 == NDT * 4 * 64, "shape");
   __shared__ u32x4 phl[2][DK * DK / 8];
   __shared__ f32x4 bl[2][NDT * 4 * 64];                     // [u][tile][lane]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = blockIdx.x % NH;
   const int h = (blockIdx.x / NH) % a.hv;
   const int seq = blockIdx.x / (NH * a.hv);
@@ -508,11 +508,11 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
     for (int p = 1; p <= last; p += 2) {
       put(p, r0);
       if (p + 2 <= last) load(p + 2, r0);
-      __syncthreads();
+      lds_barrier();
       if (p + 1 <= last) {
         put(p + 1, r1);
         if (p + 3 <= last) load(p + 3, r1);
-        __syncthreads();
+        lds_barrier();
       }
     }
     return;
@@ -526,7 +526,7 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
     for (int u = 0; u < NDT; u++) S[u] = *reinterpret_cast<const f32x4*>(s1 + state_frag<DV>(u, jt, lane));
   }
   for (int p = 1; p <= last; p++) {
-    __syncthreads();
+    lds_barrier();
     const int b = p & 1;
     f32x4 acc[NDT];
 #pragma unroll
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   constexpr int NCT = DV / 64;  // state column tiles per carry wave
   static_assert(DV % 64 == 0, "state columns must split over four waves");
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = 4 * (lane >> 4);
   int n, hk, h;
   block_unit(a, n, hk, h);
@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
       if (nch > 1) st.load(ch0 + 1);
     }
     for (int i = 0; i < nch; i++) {
-      __syncthreads();
+      lds_barrier();
       if (i + 1 < nch) st.store(sm, (i + 1) & 1);
       if (i + 2 < nch) st.load(ch0 + i + 2);
     }
@@ -607,7 +607,7 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)sg.s0 * orow + (long)h * DV;
   u32x2 ob[NCT][C / 16];
   for (int i = 0; i < nch; i++) {
-    __syncthreads();
+    lds_barrier();
     carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob);
     const int cs = (ch0 + i) * C;
     const int clen = min(C, sg.s1 - sg.s0 - cs);

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
-            "gdn_decode_step"]
+            "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step"]
 
 
 class GdnDims(ctypes.Structure):
@@ -64,6 +64,8 @@ def _load():
         "gdn_prefill_chunked": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "gdn_prefill_prepare": ([D, P, P, P, P, P, P, sz, P], i32),
         "gdn_prefill_scan": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gdn_prefill_conv_prepare": ([D, i32, P, i64, P, P, P, P, P, P, P, i64, P, sz, P], i32),
+        "gdn_prefill_conv_chunked": ([D, i32, P, i64, P, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
     }
     for name, (args, res) in sig.items():
@@ -241,6 +243,81 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, nu
         state_out = torch.empty((p.dims.num_seqs, hv, q.shape[2], dv), dtype=torch.float32, device=q.device)
     p(q, k, v, g, beta, out, state_in, state_out, stream)
     return out, state_out
+
+
+class ConvPrefill:
+    """Bound prefill from raw rows: x [N_tok, C_conv] (channels [q | k | v],
+    rows may be strided) -> y = SiLU(conv(x)) [N_tok, C_conv] -> o, state.
+    Dims + workspace, reusable across calls."""
+
+    def __init__(self, x, weight, *, num_qk_heads, num_v_heads, head_dim_k, head_dim_v, y_stride=None,
+                 cu_seqlens=None, seqlen=None, num_seqs=None, chunk_size=64, l2norm=True, heads_tiled=False,
+                 scale=1.0, bias=None, workspace=None):
+        n_tok, cc = x.shape
+        if cc != 2 * num_qk_heads * head_dim_k + num_v_heads * head_dim_v:
+            raise ValueError("x must have 2 H_k d_k + H_v d_v channels")
+        if cu_seqlens is not None:
+            num_seqs = cu_seqlens.numel() - 1
+            seqlen = 0
+        else:
+            seqlen = int(seqlen if seqlen is not None else n_tok)
+            num_seqs = int(num_seqs if num_seqs is not None else (n_tok // seqlen if seqlen else 1))
+        ys = int(y_stride if y_stride is not None else cc)
+        self.dims = make_dims(num_seqs=num_seqs, total_tokens=n_tok, seqlen=seqlen, num_qk_heads=num_qk_heads,
+                              num_v_heads=num_v_heads, head_dim_k=head_dim_k, head_dim_v=head_dim_v,
+                              chunk_size=chunk_size, dtype=_dtype_code(x), l2norm=l2norm, heads_tiled=heads_tiled,
+                              scale=scale, stride_q=ys, stride_k=ys, stride_v=ys)
+        self.y_stride = ys
+        self.weight, self.bias, self.cu_seqlens = weight, bias, cu_seqlens
+        self.width = weight.shape[1]
+        self.ws = workspace if workspace is not None else alloc_workspace(self.dims, x.device)
+        self.ws_bytes = self.ws.numel() * self.ws.element_size()
+
+    def views(self, y):
+        """q, k, v column views of y."""
+        d = self.dims
+        a = d.num_qk_heads * d.head_dim_k
+        n = y.shape[0]
+        return (y[:, :a].view(n, d.num_qk_heads, d.head_dim_k), y[:, a:2 * a].view(n, d.num_qk_heads, d.head_dim_k),
+                y[:, 2 * a:2 * a + d.num_v_heads * d.head_dim_v].view(n, d.num_v_heads, d.head_dim_v))
+
+    def conv_prepare(self, x, y, g, beta, conv_state=None, stream=None):
+        _check(lib.gdn_prefill_conv_prepare(ctypes.byref(self.dims), self.width, _ptr(x), _row_stride(x),
+                                            _ptr(self.weight), _ptr(self.bias), _ptr(conv_state), _ptr(g),
+                                            _ptr(beta), _ptr(self.cu_seqlens), _ptr(y), self.y_stride,
+                                            _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def scan(self, y, g, beta, o, state_in=None, state_out=None, stream=None):
+        q, k, v = self.views(y)
+        _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state_in), _ptr(self.cu_seqlens), _ptr(o), _ptr(state_out),
+                                    _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def __call__(self, x, y, g, beta, o, state_in=None, state_out=None, conv_state=None, stream=None):
+        _check(lib.gdn_prefill_conv_chunked(ctypes.byref(self.dims), self.width, _ptr(x), _row_stride(x),
+                                            _ptr(self.weight), _ptr(self.bias), _ptr(conv_state), _ptr(g),
+                                            _ptr(beta), _ptr(state_in), _ptr(self.cu_seqlens), _ptr(y),
+                                            self.y_stride, _ptr(o), _ptr(state_out), _ptr(self.ws), self.ws_bytes,
+                                            _stream(stream)))
+
+
+def conv_prefill(x, weight, g, beta, *, num_qk_heads, num_v_heads, head_dim_k, head_dim_v, state_in=None,
+                 conv_state=None, cu_seqlens=None, seqlen=None, num_seqs=None, chunk_size=64, l2norm=True,
+                 heads_tiled=False, scale=1.0, bias=None, want_state=True, stream=None):
+    """Prefill from raw rows x [N_tok, 2 H_k d_k + H_v d_v] through the conv
+    (+SiLU) and the chunked scan in one library call.  conv_state, if given,
+    is advanced in place.  Returns (y, o, state)."""
+    import torch
+    p = ConvPrefill(x, weight, num_qk_heads=num_qk_heads, num_v_heads=num_v_heads, head_dim_k=head_dim_k,
+                    head_dim_v=head_dim_v, cu_seqlens=cu_seqlens, seqlen=seqlen, num_seqs=num_seqs,
+                    chunk_size=chunk_size, l2norm=l2norm, heads_tiled=heads_tiled, scale=scale, bias=bias)
+    n_tok = x.shape[0]
+    y = torch.empty((n_tok, x.shape[1]), dtype=x.dtype, device=x.device)
+    o = torch.empty((n_tok, num_v_heads, head_dim_v), dtype=x.dtype, device=x.device)
+    st = torch.empty((p.dims.num_seqs, num_v_heads, head_dim_k, head_dim_v), dtype=torch.float32,
+                     device=x.device) if want_state else None
+    p(x, y, g, beta, o, state_in, st, conv_state, stream)
+    return y, o, st
 
 
 class Decode:

@@ -141,3 +141,34 @@ def test_entry_points_reject_before_any_gpu_call(g):
     assert L.gdn_decode_step(ctypes.byref(dd), 16, 16, 16, 16, 16, None, 4, None, 16, None) == 1  # no state
     assert L.gdn_prefill_scan(ctypes.byref(_dims(g, seqlen=0, total_tokens=8, num_seqs=1)), 16, 16, 16, 16, 16,
                               None, None, 16, None, 256, 1 << 30, None) == 1                    # varlen w/o cu
+
+
+def test_conv_entry_points_reject_before_any_gpu_call(g):
+    """The raw-row prefill entry points validate everything on the host."""
+    L = g.lib
+    cc = 8192
+    d = _dims(g, stride_q=cc, stride_k=cc, stride_v=cc)
+    ws = g.workspace_size(d)
+    X, Y, W, GG, B = 1 << 32, 1 << 36, 1 << 40, 1 << 41, 1 << 42   # fake, aligned, disjoint addresses
+
+    def prep(dd, width=4, x=X, sx=cc, y=Y, sy=cc, w=W, ws_ptr=256, ws_bytes=ws):
+        return L.gdn_prefill_conv_prepare(ctypes.byref(dd), width, x, sx, w, None, None, GG, B, None, y, sy,
+                                          ws_ptr, ws_bytes, None)
+
+    assert prep(_dims(g)) == 1                                   # strides of d must equal stride_y
+    assert prep(d, width=9) == 2                                 # width out of range
+    assert prep(d, width=1) == 2
+    assert prep(d, sx=cc - 8) == 1                               # stride below the channel count
+    assert prep(d, y=X) == 1                                     # x and y overlap
+    assert prep(d, y=X + 4096 * cc) == 1                         # partial overlap
+    assert prep(d, w=0) == 1                                     # no weight
+    assert prep(d, x=X + 2) == 1                                 # misaligned x
+    assert prep(d, ws_bytes=ws - 256) == 3                       # workspace too small
+    assert prep(d, ws_ptr=0) == 3
+    dd = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5, stride_q=cc, stride_k=cc, stride_v=cc)
+    assert prep(dd, ws_bytes=g.workspace_size(dd)) == 1          # varlen without cu_seqlens
+    # the one-call form checks the scan half (o, states) before queuing anything
+    assert L.gdn_prefill_conv_chunked(ctypes.byref(d), 4, X, cc, W, None, None, GG, B, None, None, Y, cc, None,
+                                      None, 256, ws, None) == 1
+    assert L.gdn_prefill_conv_chunked(ctypes.byref(d), 4, X, cc, W, None, None, GG, B, 8, None, Y, cc, 1 << 43,
+                                      None, 256, ws, None) == 1  # misaligned state_in
