@@ -215,13 +215,17 @@ __device__ __forceinline__ f32x4 inv16(const float* A0, int L, int lane) {
   return mm_tt(id + n8t, x2);                 // (I + N^8) x2
 }
 
+// Waves per prepare workgroup.
+constexpr int kPrepWaves = 8;
+
 template <class E, int C, int DK, int HPW>
-__global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
+__global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
+  constexpr int PW = kPrepWaves, PT = 64 * kPrepWaves;
   typedef typename E::store_t T;
   typedef PrepSmem<E, C, DK, HPW> SM;
   constexpr int NRT = C / 16;
   constexpr int NT = NRT * (NRT + 1) / 2;      // lower 16x16 tiles (diagonal included)
-  constexpr int NTW = (NT + 3) / 4;            // per wave
+  constexpr int NTW = (NT + PW - 1) / PW;      // per wave
   constexpr int L = SM::ALD;
   __shared__ SM sm;
   // one-dimensional grid: workgroup = (chunk, q/k head with HPW of its v-heads)
@@ -243,20 +247,20 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   // gates; all loads are issued before any is used
   constexpr int EPV = 16 / sizeof(T);
   constexpr int VPR = DK / EPV;  // 16-byte vectors per row
-  constexpr int NV = 2 * C * VPR / 256;
-  static_assert(NV * 256 == 2 * C * VPR, "K/Q staging must tile the workgroup");
+  constexpr int KQV = 2 * C * VPR;               // 16-byte vectors of K and Q
+  constexpr int NV = (KQV + PT - 1) / PT;
   u32x4 w[NV];
   {
     const T* kp = reinterpret_cast<const T*>(a.k);
     const T* qp = reinterpret_cast<const T*>(a.q);
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-      const int idx = tid + 256 * j;
+      const int idx = tid + PT * j;
       const int which = idx / (C * VPR);
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
       w[j] = u32x4{0u, 0u, 0u, 0u};
-      if (r < len) {
+      if (idx < KQV && r < len) {
         const T* src = which ? qp + (long)(start + r) * a.stride_q : kp + (long)(start + r) * a.stride_k;
         w[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
       }
@@ -272,11 +276,11 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   {
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-      const int idx = tid + 256 * j;
+      const int idx = tid + PT * j;
       const int which = idx / (C * VPR);
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
-      *reinterpret_cast<u32x4*>(which ? &sm.u.in.q[r][cv * EPV] : &sm.u.in.k[r][cv * EPV]) = w[j];
+      if (idx < KQV) *reinterpret_cast<u32x4*>(which ? &sm.u.in.q[r][cv * EPV] : &sm.u.in.k[r][cv * EPV]) = w[j];
       const T* e = reinterpret_cast<const T*>(&w[j]);
       float ss = 0.f;
 #pragma unroll
@@ -285,7 +289,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
         ss += x * x;
       }
       ss = group_sum<VPR>(ss);
-      if (cv == 0) {
+      if (cv == 0 && idx < KQV) {
         const float inv = a.l2norm ? __builtin_amdgcn_rsqf(ss + kL2Eps) : 1.0f;
         if (which) sm.rq[r] = a.scale * inv; else sm.rk[r] = inv;
       }
@@ -311,7 +315,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   f32x4 rawA[NTW];
 #pragma unroll
   for (int n = 0; n < NTW; n++) {
-    const int t = wave + 4 * n;
+    const int t = wave + PW * n;
     if (t < NT) {
       int i, j;
       tile_ij(t, i, j);
@@ -319,7 +323,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
       rawA[n] = tile_mma<E, DK>(acc, &sm.u.in.k[16 * j][0], SM::KLD, &sm.u.in.k[16 * i][0], SM::KLD, lane);
     }
   }
-  for (int t = wave; t < NT; t += 4) {
+  for (int t = wave; t < NT; t += PW) {
     int i, j;
     tile_ij(t, i, j);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -344,7 +348,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
     }
   }
   // upper tiles of P are zero (the scan reads P in whole 32-column steps)
-  for (int t = wave; t < NRT * NRT; t += 4) {
+  for (int t = wave; t < NRT * NRT; t += PW) {
     const int i = t / NRT, j = t % NRT;
     if (j <= i) continue;
     const int r = 16 * i + c16, s0 = 16 * j + r4;
@@ -371,7 +375,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   lds_barrier();  // K and Q are dead: A takes their place
 #pragma unroll
   for (int n = 0; n < NTW; n++) {
-    const int t = wave + 4 * n;
+    const int t = wave + PW * n;
     if (t < NT) {
       int i, j;
       tile_ij(t, i, j);
@@ -392,7 +396,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   }
   lds_barrier();
   // ---- diagonal 16x16 blocks, inverted in registers, written back in place
-  for (int blk = wave; blk < HPW * NRT; blk += 4) {
+  for (int blk = wave; blk < HPW * NRT; blk += PW) {
     const int hh = blk / NRT, d = blk % NRT;
     float* A0 = &sm.u.at[hh][16 * d][16 * d];
     const f32x4 inv = inv16(A0, L, lane);
@@ -401,7 +405,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
   lds_barrier();
   // ---- merge 16 -> 32: [[X, 0], [Y, Z]]^{-1} has lower-left block -Z (Y X)
   if constexpr (C >= 32) {
-    for (int m = wave; m < HPW * (NRT / 2); m += 4) {
+    for (int m = wave; m < HPW * (NRT / 2); m += PW) {
       const int hh = m / (NRT / 2), b = 32 * (m % (NRT / 2));
       float* at = &sm.u.at[hh][0][0];
       const f32x4 w = mm_tt(ld_ct(at + (b + 16) * L + b, L, lane), ld_c(at + b * L + b, L, lane));
@@ -444,7 +448,7 @@ __global__ void __launch_bounds__(256) k_prepare(ScanArgs a) {
 #pragma unroll
   for (int hh = 0; hh < HPW; hh++) {
     T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);
-    for (int idx = tid; idx < C * C / 4; idx += 256) {
+    for (int idx = tid; idx < C * C / 4; idx += PT) {
       const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0]);
       f32x4 v;
@@ -768,7 +772,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
 template <class E, int C, int DK>
 hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
   const int G = a.hv / a.hk;
-  const dim3 block(256);
+  const dim3 block(64 * kPrepWaves);
   const int hpw = G % 2 == 0 ? 2 : 1;
   const dim3 grid((unsigned)((long)a.max_chunks * (a.hv / hpw)));  // one (chunk, head group) per workgroup
   if (hpw == 2) hipLaunchKernelGGL((k_prepare<E, C, DK, 2>), grid, block, 0, s, a);

@@ -448,25 +448,33 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
 
 // ----------------------------------------------------------------- combine
 // S_start[p+1] = Phi_p S_start[p] + B_p for p = 1 .. nseg-2, in place over
-// B_p.  One workgroup per (sequence, v-head, 64 state columns), eight waves:
-//  - waves 0..3 each own one 16-column tile of S (all rows) in accumulators,
-//    so S feeds the matrix cores straight from registers; they only store;
-//  - waves 4..7 only load: Phi_p and the B_p columns, two steps ahead in two
+// B_p.  The chain is separable by state columns: one workgroup per
+// (sequence, v-head, CW 16-column tiles), CW + LW waves:
+//  - waves 0..CW-1 each own one 16-column tile of S (all rows) in
+//    accumulators, so S feeds the matrix cores straight from registers; they
+//    only store;
+//  - waves CW.. only load: Phi_p and the B_p columns, two steps ahead in two
 //    register sets, into a two-slot LDS ring.
 // Keeping loads and stores in different waves means no wait for a load ever
-// has to wait for a store to be acknowledged.
-template <int DK, int DV>
-__global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
-  constexpr int NDT = DK / 16, KS = DK / 32, NH = DV / 64;  // column halves of 64
-  constexpr int PV = DK * DK / 8 / 256;                    // 16-byte words of Phi per loader thread
-  constexpr int BV = NDT * 4 * 64 / 256;                   // f32x4 words of B per loader thread
-  static_assert(PV * 256 * 8 == DK * DK && BV * 256 == NDT * 4 * 64, "shape");
+// has to wait for a store to be acknowledged.  The column groups of one
+// v-head get the same blockIdx % 8, i.e. the same XCD, and share its L2 for
+// the transitions.
+template <int DK, int DV, int CW, int LW>
+__global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
+  constexpr int NDT = DK / 16, KS = DK / 32;
+  constexpr int NG = DV / (16 * CW);                        // column groups per v-head
+  constexpr int LT = 64 * LW;                               // loader threads
+  constexpr int PV = DK * DK / 8 / LT;                      // 16-byte words of Phi per loader thread
+  constexpr int BV = NDT * CW * 64 / LT;                    // f32x4 words of B per loader thread
+  static_assert(PV * LT * 8 == DK * DK && BV * LT == NDT * CW * 64, "shape");
   __shared__ u32x4 phl[2][DK * DK / 8];
-  __shared__ f32x4 bl[2][NDT * 4 * 64];                     // [u][tile][lane]
+  __shared__ f32x4 bl[2][NDT * CW * 64];                    // [u][tile][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int half = blockIdx.x % NH;
-  const int h = (blockIdx.x / NH) % a.hv;
-  const int seq = blockIdx.x / (NH * a.hv);
+  const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
+  const int grp = m8 % NG;                                  // column group
+  const int unit = (m8 / NG) * 8 + xcd;                     // (sequence, v-head)
+  const int h = unit % a.hv;
+  const int seq = unit / a.hv;
   if (seq >= a.num_seqs) return;
   int nseg, sbase;
   if (a.seqlen > 0) {
@@ -480,8 +488,8 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
   const int last = nseg - 2;  // steps p = 1 .. last
   auto sptr = [&](int p) { return a.seg_state + ((long)(sbase + p) * a.hv + h) * DK * DV; };
 
-  if (wave >= 4) {
-    const int lt = tid - 256;
+  if (wave >= CW) {
+    const int lt = tid - 64 * CW;
     struct Set {
       u32x4 pf[PV];
       f32x4 bf[BV];
@@ -489,19 +497,19 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
     auto load = [&](int p, Set& r) {  // Phi_p and B_p (held in S_start[p+1])
       const u32x4* ph = reinterpret_cast<const u32x4*>(a.seg_phi + ((long)(sbase + p) * a.hv + h) * DK * DK);
 #pragma unroll
-      for (int i = 0; i < PV; i++) r.pf[i] = ph[lt + 256 * i];
+      for (int i = 0; i < PV; i++) r.pf[i] = ph[lt + LT * i];
       const float* b = sptr(p + 1);
 #pragma unroll
       for (int i = 0; i < BV; i++) {
-        const int w = lt + 256 * i, u = w / 256, t = (w / 64) % 4, l = w % 64;
-        r.bf[i] = *reinterpret_cast<const f32x4*>(b + state_frag<DV>(u, 4 * half + t, l));
+        const int w = lt + LT * i, u = w / (64 * CW), t = (w / 64) % CW, l = w % 64;
+        r.bf[i] = *reinterpret_cast<const f32x4*>(b + state_frag<DV>(u, CW * grp + t, l));
       }
     };
     auto put = [&](int p, Set& r) {
 #pragma unroll
-      for (int i = 0; i < PV; i++) phl[p & 1][lt + 256 * i] = r.pf[i];
+      for (int i = 0; i < PV; i++) phl[p & 1][lt + LT * i] = r.pf[i];
 #pragma unroll
-      for (int i = 0; i < BV; i++) bl[p & 1][lt + 256 * i] = r.bf[i];
+      for (int i = 0; i < BV; i++) bl[p & 1][lt + LT * i] = r.bf[i];
     };
     load(1, r0);
     if (last >= 2) load(2, r1);
@@ -518,7 +526,7 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
     return;
   }
 
-  const int jt = 4 * half + wave;  // this wave's column tile
+  const int jt = CW * grp + wave;  // this wave's column tile
   f32x4 S[NDT];
   {
     const float* s1 = sptr(1);
@@ -530,7 +538,7 @@ __global__ void __launch_bounds__(512) k_seg_combine(ScanArgs a) {
     const int b = p & 1;
     f32x4 acc[NDT];
 #pragma unroll
-    for (int u = 0; u < NDT; u++) acc[u] = bl[b][(u * 4 + wave) * 64 + lane];
+    for (int u = 0; u < NDT; u++) acc[u] = bl[b][(u * CW + wave) * 64 + lane];
 #pragma unroll
     for (int m = 0; m < KS; m++) {
       const bf16x8 zb = frag_acc(S[2 * m], S[2 * m + 1]);
@@ -633,6 +641,9 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   }
 }
 
+// State-column tiles (16 columns each) per combine workgroup.
+constexpr int kCombineWaves = 1;
+
 template <int C, int DK, int DV>
 hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   const int G = a.hv / a.hk;
@@ -642,7 +653,11 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_seg_pass1<C, DK, DV, NW1>), grid, dim3(64 * NW1), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_seg_combine<DK, DV>), dim3(a.num_seqs * a.hv * (DV / 64)), dim3(512), 0, s, a);
+  {
+    constexpr int CW = kCombineWaves, LW = 4, NG = DV / (16 * CW);
+    const int units = a.num_seqs * a.hv;
+    hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, LW>), dim3(8 * ((units + 7) / 8) * NG), dim3(64 * (CW + LW)), 0, s, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((k_seg_pass2<C, DK, DV>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
