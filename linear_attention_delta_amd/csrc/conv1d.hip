@@ -149,8 +149,12 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
           if constexpr (ACT && std::is_same<E, BF16>::value) out[i] = conv_sum<W>(bias[i], w[i], xv);
           else out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
         }
-        if constexpr (ACT && std::is_same<E, BF16>::value) silu8_for_bf16(out);
-        Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
+        if constexpr (ACT && std::is_same<E, BF16>::value) {
+          silu8_for_bf16(out);
+          *reinterpret_cast<u32x4*>(y + (long)(t_begin + p) * a.stride_y + c0) = conv_pack_bf16x8_canonical(out);
+        } else {
+          Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
+        }
       }
       if (r + 1 < RUN) {
 #pragma unroll

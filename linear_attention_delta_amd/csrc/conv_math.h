@@ -69,8 +69,14 @@ __device__ __forceinline__ void silu8_for_bf16(float (&v)[8]) {
   }
   if (any) {
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-      if (silu_needs_exact(v[i], q[i])) q[i] = silu_exact(v[i]);
+    for (int i = 0; i < 8; i++) {
+      if (silu_needs_exact(v[i], q[i])) {
+        // NaN can only arise here (every NaN or -inf input is flagged): make
+        // it the canonical quiet NaN, so the rounding below needs no check
+        const float e = silu_exact(v[i]);
+        q[i] = e != e ? __uint_as_float(0x7fc00000u) : e;
+      }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; i++) v[i] = q[i];
@@ -94,6 +100,16 @@ __device__ __forceinline__ float conv_sum(float bias, const float (&w)[W], const
 #pragma unroll
   for (int j = 0; j < W; j++) acc = __builtin_fmaf(w[j], xv[j], acc);
   return acc;
+}
+
+// Eight outputs rounded to bf16 with the hardware conversion (nearest even),
+// for values that are finite, infinite or the canonical quiet NaN (which
+// converts to 0x7fc0): the outputs of silu8_for_bf16.
+__device__ __forceinline__ u32x4 conv_pack_bf16x8_canonical(const float* v) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; i++) w[i] = cvt_bf16x2(v[2 * i], v[2 * i + 1]);
+  return w;
 }
 
 // Eight outputs rounded to bf16 (nearest even with the hardware conversion;
