@@ -138,9 +138,11 @@ gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen,
 /*
  * Device workspace (bytes) that gdn_prefill_chunked / gdn_prefill_prepare /
  * gdn_prefill_scan need for this problem: per chunk and v-head the inverse
- * Tt, the score matrix P (both C x C in the q/k/v dtype) and four C-vectors
- * of fp32 scale factors, plus the chunk table for varlen input.  0 on invalid
- * dims (gdn_last_error says why).
+ * Tt and room for the score matrix P (both C x C in the q/k/v dtype) and
+ * eight C-vectors of fp32 per-token factors, plus the chunk table for varlen
+ * input; for bf16 with chunk 32 or 64 also, per carry segment and v-head,
+ * an fp32 start state and a bf16 d_k x d_k transition (and a segment table
+ * for varlen input).  0 on invalid dims (gdn_last_error says why).
  */
 size_t gdn_prefill_workspace_size(const gdn_dims *d);
 

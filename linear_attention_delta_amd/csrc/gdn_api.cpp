@@ -147,7 +147,7 @@ WsLayout ws_layout(const gdn_dims* d) {
   w.mats_off = w.table_bytes;
   w.mats_bytes = align256(units * 2 * C * C * elem_size(d->dtype));
   w.scal_off = w.mats_off + w.mats_bytes;
-  w.scal_bytes = align256(units * 4 * C * 4);
+  w.scal_bytes = align256(units * gdn::kScalRows * C * 4);
   w.segt_off = w.scal_off + w.scal_bytes;
   w.segt_bytes = w.sst_bytes = w.phi_bytes = 0;
   if (seg_enabled(d)) {

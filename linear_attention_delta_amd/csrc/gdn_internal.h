@@ -21,6 +21,15 @@ struct ConvArgs {
   long stride_y;
 };
 
+// Rows of the per-(chunk, v-head) scalar block written by the prepare, each
+// `chunk` fp32 values, one per token of the chunk:
+//   0 a = e^{gamma} rk      1 b = scale e^{gamma} rq (sequential carry only)
+//   2 c = e^{gamma_last - gamma} rk                  3 e^{gamma_last} (first element)
+//   4 gamma                 5 rk = 1/|k| (1 without the L2 norm)
+//   6 (free: the segment-parallel carry puts scale rq there in LDS)
+//   7 e^{gamma}
+constexpr int kScalRows = 8;
+
 // Everything the scan kernels need; pointers are device pointers.
 struct ScanArgs {
   int num_seqs, total_tokens, seqlen;  // seqlen > 0: dense
@@ -41,7 +50,7 @@ struct ScanArgs {
   // workspace carve-up
   int32_t* chunk_offsets;     // [num_seqs + 1], varlen only
   void* tinv;                 // [max_chunks][hv][2][chunk][chunk] in the operand type: Tt, P
-  float* scal;                // [max_chunks][hv][4][chunk] fp32: a, b, c, e^{gamma_last}
+  float* scal;                // [max_chunks][hv][kScalRows][chunk] fp32 per-row scalars (see kScalRows)
   int max_chunks;
   // segment-parallel scan (bf16, chunk 32/64): every sequence is cut into
   // segments of seg_len chunks (at least one segment per sequence)

@@ -218,7 +218,10 @@ __device__ __forceinline__ f32x4 inv16(const float* A0, int L, int lane) {
 // Waves per prepare workgroup.
 constexpr int kPrepWaves = 8;
 
-template <class E, int C, int DK, int HPW>
+// WQ: also stage Q and write P and b (what the sequential carry reads); the
+// segment-parallel carry forms P itself from Q and K, so without WQ only K
+// is read and P is not written.
+template <class E, int C, int DK, int HPW, bool WQ>
 __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
   constexpr int PW = kPrepWaves, PT = 64 * kPrepWaves;
   typedef typename E::store_t T;
@@ -247,7 +250,7 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
   // gates; all loads are issued before any is used
   constexpr int EPV = 16 / sizeof(T);
   constexpr int VPR = DK / EPV;  // 16-byte vectors per row
-  constexpr int KQV = 2 * C * VPR;               // 16-byte vectors of K and Q
+  constexpr int KQV = (WQ ? 2 : 1) * C * VPR;    // 16-byte vectors of K (and Q)
   constexpr int NV = (KQV + PT - 1) / PT;
   u32x4 w[NV];
   {
@@ -323,6 +326,7 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
       rawA[n] = tile_mma<E, DK>(acc, &sm.u.in.k[16 * j][0], SM::KLD, &sm.u.in.k[16 * i][0], SM::KLD, lane);
     }
   }
+  if constexpr (WQ) {
   for (int t = wave; t < NT; t += PW) {
     int i, j;
     tile_ij(t, i, j);
@@ -362,15 +366,19 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
       }
     }
   }
+  }
   // ---- per-token scalars a, b, c and e^{gamma_last}
   if (wave < HPW && lane < C) {
-    float* scal = a.scal + (chunk * a.hv + hs[wave]) * (4 * C);
+    float* scal = a.scal + (chunk * a.hv + hs[wave]) * (kScalRows * C);
     const float gm = sm.gam[wave][lane], glast = sm.gam[wave][C - 1];
     const float eg = __expf(gm);
     scal[lane] = eg * sm.rk[lane];
-    scal[C + lane] = eg * sm.rq[lane];
+    if constexpr (WQ) scal[C + lane] = eg * sm.rq[lane];
     scal[2 * C + lane] = __expf(glast - gm) * sm.rk[lane];
     scal[3 * C + lane] = lane == 0 ? __expf(glast) : 0.f;
+    scal[4 * C + lane] = gm;
+    scal[5 * C + lane] = sm.rk[lane];
+    scal[7 * C + lane] = eg;
   }
   lds_barrier();  // K and Q are dead: A takes their place
 #pragma unroll
@@ -658,7 +666,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       if (r < clen)
         pv = *reinterpret_cast<const u32x4*>(vp + (long)(cs + r) * a.stride_v + (long)h * a.dv + dv0 + cv * EPV);
     }
-    if (tid < S_V) ps = *reinterpret_cast<const u32x4*>(scp + blk * (4 * C) + tid * 4);
+    if (tid < S_V) ps = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + tid * 4);
   };
 
   auto store_chunk = [&](int b) {
@@ -775,8 +783,13 @@ hipError_t launch_prepare_t(const ScanArgs& a, hipStream_t s) {
   const dim3 block(64 * kPrepWaves);
   const int hpw = G % 2 == 0 ? 2 : 1;
   const dim3 grid((unsigned)((long)a.max_chunks * (a.hv / hpw)));  // one (chunk, head group) per workgroup
-  if (hpw == 2) hipLaunchKernelGGL((k_prepare<E, C, DK, 2>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_prepare<E, C, DK, 1>), grid, block, 0, s, a);
+  if (seg_path(a)) {
+    if (hpw == 2) hipLaunchKernelGGL((k_prepare<E, C, DK, 2, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_prepare<E, C, DK, 1, false>), grid, block, 0, s, a);
+  } else {
+    if (hpw == 2) hipLaunchKernelGGL((k_prepare<E, C, DK, 2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_prepare<E, C, DK, 1, true>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

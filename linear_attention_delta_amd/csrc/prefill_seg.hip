@@ -119,7 +119,7 @@ struct alignas(16) SegSmem {
   uint16_t k[2][C][KLD];
   uint16_t v[2][C][VLD];
   uint16_t tt[2][C][CLD];
-  float sc[2][4][C];                   // a, b, c, e^{gamma_last}
+  float sc[2][OUT ? kScalRows : 4][C];  // per-row scalars (rows as in the workspace; pass 2 puts scale rq in row 6)
   uint16_t q[OUT ? 2 : 1][OUT ? C : 1][KLD];
   uint16_t p[OUT ? 2 : 1][OUT ? C : 1][CLD];
 };
@@ -131,12 +131,12 @@ struct Stager {
   typedef SegSmem<C, DK, DV, OUT> SM;
   static constexpr int KV = C * DK / 8, VV = C * DV / 8, TV = C * C / 8;  // 16-byte vectors
   static constexpr int NK = (KV + NTH - 1) / NTH, NV = (VV + NTH - 1) / NTH, NT = (TV + NTH - 1) / NTH;
-  u32x4 rk[NK], rq[OUT ? NK : 1], rv[NV], rt[NT], rp[OUT ? NT : 1], rs;
-  float rbq[OUT ? NK : 1];  // b of each staged Q row: Q is stored as diag(b) Q
+  u32x4 rk[NK], rq[OUT ? NK : 1], rv[NV], rt[NT], rs;
   const uint16_t *kp, *qp, *vp, *mp;
   const float* sp;
   long sk, sq, sv, mstep, sstep;
-  int ntok, tid;
+  int ntok, tid, l2norm;
+  float scale;
 
   __device__ __forceinline__ void load(int ch) {  // ch: chunk index within the sequence
     const int cs = ch * C;
@@ -146,10 +146,8 @@ struct Stager {
       const int idx = tid + NTH * j, r = idx / (DK / 8), cv = idx % (DK / 8);
       const bool ok = idx < KV && r < clen;
       rk[j] = ok ? *reinterpret_cast<const u32x4*>(kp + (long)(cs + r) * sk + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (OUT) {
+      if constexpr (OUT)
         rq[j] = ok ? *reinterpret_cast<const u32x4*>(qp + (long)(cs + r) * sq + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
-        rbq[j] = idx < KV ? sp[ch * sstep + C + r] : 0.f;
-      }
     }
 #pragma unroll
     for (int j = 0; j < NV; j++) {
@@ -161,12 +159,10 @@ struct Stager {
 #pragma unroll
     for (int j = 0; j < NT; j++) {
       const int idx = tid + NTH * j;
-      if (idx < TV) {
-        rt[j] = *reinterpret_cast<const u32x4*>(mc + 8 * idx);
-        if constexpr (OUT) rp[j] = *reinterpret_cast<const u32x4*>(mc + C * C + 8 * idx);
-      }
+      if (idx < TV) rt[j] = *reinterpret_cast<const u32x4*>(mc + 8 * idx);
     }
-    if (tid < C) rs = *reinterpret_cast<const u32x4*>(sp + ch * sstep + 4 * tid);
+    // scalar rows 0..3 (and 4..7 with outputs)
+    if (tid < (OUT ? 2 : 1) * C) rs = *reinterpret_cast<const u32x4*>(sp + ch * sstep + 4 * tid);
   }
 
   __device__ __forceinline__ void store(SM& sm, int b) const {
@@ -177,13 +173,22 @@ struct Stager {
         *reinterpret_cast<u32x2*>(&sm.k[b][r][lo]) = u32x2{rk[j][0], rk[j][1]};
         *reinterpret_cast<u32x2*>(&sm.k[b][r][lo + 8]) = u32x2{rk[j][2], rk[j][3]};
         if constexpr (OUT) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            w[e] = cvt_bf16x2(rbq[j] * __uint_as_float(rq[j][e] << 16), rbq[j] * __uint_as_float(rq[j][e] & 0xffff0000u));
-          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo]) = u32x2{w[0], w[1]};
-          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo + 8]) = u32x2{w[2], w[3]};
+          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo]) = u32x2{rq[j][0], rq[j][1]};
+          *reinterpret_cast<u32x2*>(&sm.q[b][r][lo + 8]) = u32x2{rq[j][2], rq[j][3]};
         }
+      }
+      if constexpr (OUT) {
+        // scale / |q_r| (row 6): the DK/8 words of a row sit in consecutive lanes
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float x0 = __uint_as_float(rq[j][e] << 16), x1 = __uint_as_float(rq[j][e] & 0xffff0000u);
+          ss += x0 * x0;
+          ss += x1 * x1;
+        }
+        ss = group_sum<DK / 8>(ss);
+        if (idx < KV && idx % (DK / 8) == 0)
+          sm.sc[b][6][r] = scale * (l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f);
       }
     }
 #pragma unroll
@@ -197,25 +202,22 @@ struct Stager {
       if (idx < TV) {
         *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo]) = u32x2{rt[j][0], rt[j][1]};
         *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo + 8]) = u32x2{rt[j][2], rt[j][3]};
-        if constexpr (OUT) {
-          *reinterpret_cast<u32x2*>(&sm.p[b][r][lo]) = u32x2{rp[j][0], rp[j][1]};
-          *reinterpret_cast<u32x2*>(&sm.p[b][r][lo + 8]) = u32x2{rp[j][2], rp[j][3]};
-        }
       }
     }
-    if (tid < C) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + 4 * tid) = rs;
+    // row 6 is this stager's own (scale rq, above)
+    if (tid < (OUT ? 2 : 1) * C && (4 * tid) / C != 6) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + 4 * tid) = rs;
   }
 };
 
 // One chunk of the carry for the NCT 16-column tiles of Z owned by this
 // wave (tile j is state column tile col[j]; vcol[j] < 0 marks a transition
 // tile, whose values term is zero).  Z <- e^{gl} Z + K^T diag(c) Tt (V -
-// diag(a) K Z).  With OUT, also O^T = Z^T (diag(b) Q)^T + U^T P^T (the staged Q
-// rows already carry b), returned in
+// diag(a) K Z).  With OUT, also O^T = (Z^T Q^T) diag(b) + U^T P^T, returned in
 // ob as bf16: lane (c16, g) holds columns 4g..4g+3 of tile j for token 16t+c16.
-template <int C, int DK, int DV, int NCT, bool OUT>
+// mid() runs after the state update, before P is read.
+template <int C, int DK, int DV, int NCT, bool OUT, class Mid>
 __device__ __forceinline__ void carry_chunk(SegSmem<C, DK, DV, OUT>& sm, int b, f32x4 (&Z)[DK / 16][NCT],
-                                            const int (&vcol)[NCT], int lane, u32x2 (&ob)[NCT][C / 16]) {
+                                            const int (&vcol)[NCT], int lane, u32x2 (&ob)[NCT][C / 16], Mid mid) {
   typedef SegSmem<C, DK, DV, OUT> SM;
   constexpr int NRT = C / 16, PS = C / 32, KS = DK / 32, NDT = DK / 16;
   const int c16 = lane & 15, g = lane >> 4, r4 = 4 * g;
@@ -273,10 +275,13 @@ __device__ __forceinline__ void carry_chunk(SegSmem<C, DK, DV, OUT>& sm, int b, 
     }
   }
 
+  // With OUT: O^T = (Z^T Q^T) diag(b) + U^T P^T, b = (scale rq) e^{gamma}; lane
+  // (c16, g) holds 4 consecutive columns 4g..4g+3 of token 16t + c16.  Only
+  // the last term needs P, so it comes after mid() and after the state
+  // update; the unscaled U is kept as operand fragments for it.
+  f32x4 Y[OUT ? NCT : 1][OUT ? NRT : 1];
+  bf16x8 uo[OUT ? PS : 1][NCT];
   if constexpr (OUT) {
-    // O^T = Z^T (diag(b) Q)^T + U^T P^T; lane (c16, g) holds 4 consecutive
-    // columns 4g..4g+3 of token 16t + c16
-    f32x4 Y[NCT][NRT];
 #pragma unroll
     for (int j = 0; j < NCT; j++)
 #pragma unroll
@@ -290,21 +295,15 @@ __device__ __forceinline__ void carry_chunk(SegSmem<C, DK, DV, OUT>& sm, int b, 
         for (int j = 0; j < NCT; j++) Y[j][t] = mfma16(zb[m][j], bq, Y[j][t]);
       }
 #pragma unroll
-    for (int pp = 0; pp < PS; pp++) {
-      bf16x8 ub[NCT];
+    for (int t = 0; t < NRT; t++) {
+      const float bt = sm.sc[b][6][16 * t + c16] * sm.sc[b][7][16 * t + c16];
 #pragma unroll
-      for (int j = 0; j < NCT; j++) ub[j] = frag_acc(U[2 * pp][j], U[2 * pp + 1][j]);
-#pragma unroll
-      for (int t = 2 * pp; t < NRT; t++) {
-        const bf16x8 bp = ld_frag(&sm.p[b][16 * t + c16][32 * pp + 8 * g]);
-#pragma unroll
-        for (int j = 0; j < NCT; j++) Y[j][t] = mfma16(ub[j], bp, Y[j][t]);
-      }
+      for (int j = 0; j < NCT; j++) Y[j][t] = bt * Y[j][t];
     }
 #pragma unroll
-    for (int j = 0; j < NCT; j++)
+    for (int pp = 0; pp < PS; pp++)
 #pragma unroll
-      for (int t = 0; t < NRT; t++) ob[j][t] = pack4_bf16(Y[j][t]);
+      for (int j = 0; j < NCT; j++) uo[pp][j] = frag_acc(U[2 * pp][j], U[2 * pp + 1][j]);
   }
 
   // Z <- e^{gamma_last} Z + K^T (diag(c) U)
@@ -333,6 +332,66 @@ __device__ __forceinline__ void carry_chunk(SegSmem<C, DK, DV, OUT>& sm, int b, 
       for (int j = 0; j < NCT; j++) Z[u][j] = mfma16(akt, ub[j], Z[u][j]);
     }
   }
+
+  mid();  // pass 2: P of this chunk is ready in LDS after this
+  if constexpr (OUT) {
+#pragma unroll
+    for (int pp = 0; pp < PS; pp++) {
+#pragma unroll
+      for (int t = 2 * pp; t < NRT; t++) {
+        const bf16x8 bp = ld_frag(&sm.p[b][16 * t + c16][32 * pp + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < NCT; j++) Y[j][t] = mfma16(uo[pp][j], bp, Y[j][t]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int t = 0; t < NRT; t++) ob[j][t] = pack4_bf16(Y[j][t]);
+  }
+}
+
+// P of the chunk in LDS buffer b, formed by the NSW staging waves (sw = this
+// wave among them) from the staged K and raw Q and the row scalars:
+//   P[r][s] = (scale rq_r) rk_s e^{gamma_r - gamma_s} q_r . k_s   (s <= r), else 0,
+// in the carry's operand layout: row r, column s at the permuted position.
+// Tiles (t, j) with j <= t are products; the upper tiles (t even, j = t + 1)
+// that a 32-wide k step also reads are written as zero.  Each tile is
+// D = K_j Q_t^T on the matrix cores, so lane (c16, g) holds P[16t + c16][16j + 4g + e]:
+// 4 consecutive columns, one 8-byte store.
+template <int C, int DK, int DV, int NSW>
+__device__ __forceinline__ void compute_p(SegSmem<C, DK, DV, true>& sm, int b, int sw, int lane) {
+  constexpr int NRT = C / 16, KS = DK / 32;
+  constexpr int NLOW = NRT * (NRT + 1) / 2, NZ = NRT / 2;
+  const int c16 = lane & 15, g = lane >> 4, r4 = 4 * g;
+  for (int n = sw; n < NLOW + NZ; n += NSW) {
+    int t, j;
+    bool zero = n >= NLOW;
+    if (!zero) {
+      t = 0;
+      while ((t + 1) * (t + 2) / 2 <= n) t++;
+      j = n - t * (t + 1) / 2;
+    } else {
+      t = 2 * (n - NLOW);
+      j = t + 1;
+    }
+    const int r = 16 * t + c16, s0 = 16 * j + r4;
+    u32x2 w = {0u, 0u};
+    if (!zero) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; m++)
+        acc = mfma16(ld_frag(&sm.k[b][16 * j + c16][32 * m + 8 * g]), ld_frag(&sm.q[b][r][32 * m + 8 * g]), acc);
+      const float fr = sm.sc[b][6][r], gr = sm.sc[b][4][r];
+      const f32x4 rks = ld4(&sm.sc[b][5][s0]), gs = ld4(&sm.sc[b][4][s0]);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? fr * rks[e] * __expf(gr - gs[e]) * acc[e] : 0.f;
+      w = pack4_bf16(v);
+    }
+    // logical columns s0..s0+3 sit together at 32(j/2) + 8g + 4(j%2)
+    *reinterpret_cast<u32x2*>(&sm.p[b][r][32 * (j >> 1) + 8 * g + 4 * (j & 1)]) = w;
+  }
 }
 
 // Set up a stager for (segment g, heads hk / h).
@@ -348,9 +407,11 @@ __device__ __forceinline__ void init_stager(Stager<C, DK, DV, OUT, NTH>& st, con
   st.qp = reinterpret_cast<const uint16_t*>(a.q) + (long)sg.s0 * a.stride_q + (long)hk * DK;
   st.vp = reinterpret_cast<const uint16_t*>(a.v) + (long)sg.s0 * a.stride_v + (long)h * DV;
   st.mp = reinterpret_cast<const uint16_t*>(a.tinv) + ((long)sg.cbase * a.hv + h) * (2 * C * C);
-  st.sp = a.scal + ((long)sg.cbase * a.hv + h) * (4 * C);
+  st.sp = a.scal + ((long)sg.cbase * a.hv + h) * (kScalRows * C);
   st.mstep = (long)a.hv * (2 * C * C);
-  st.sstep = (long)a.hv * (4 * C);
+  st.sstep = (long)a.hv * (kScalRows * C);
+  st.l2norm = a.l2norm;
+  st.scale = a.scale;
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -405,7 +466,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
     const int b = i & 1;
     if (i + 1 < nch) st.store(sm, b ^ 1);
     if (i + 2 < nch) st.load(ch0 + i + 2);
-    carry_chunk<C, DK, DV, NCT, false>(sm, b, Z, vcol, lane, ob);
+    carry_chunk<C, DK, DV, NCT, false>(sm, b, Z, vcol, lane, ob, [] {});
   }
 
   // B_p (or the true end state of the first segment) is the next segment's
@@ -557,8 +618,9 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
 
 // ------------------------------------------------------------------ pass 2
 // Eight waves: 0..3 carry the state (NCT column tiles each) and write the
-// outputs, 4..7 stage the chunks.  The staging registers live only in the
-// staging waves, so the carry keeps its accumulators in VGPRs.
+// outputs, 4..7 stage the chunks and form each chunk's P while the carry
+// works up to its last product, which waits for P at a second barrier.  The staging registers live only
+// in the staging waves, so the carry keeps its accumulators in VGPRs.
 template <int C, int DK, int DV>
 __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   typedef SegSmem<C, DK, DV, true> SM;
@@ -588,6 +650,8 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
     }
     for (int i = 0; i < nch; i++) {
       lds_barrier();
+      compute_p<C, DK, DV, 4>(sm, i & 1, wave - 4, lane);
+      lds_barrier();  // P ready for the carry's last product
       if (i + 1 < nch) st.store(sm, (i + 1) & 1);
       if (i + 2 < nch) st.load(ch0 + i + 2);
     }
@@ -616,7 +680,7 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   u32x2 ob[NCT][C / 16];
   for (int i = 0; i < nch; i++) {
     lds_barrier();
-    carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob);
+    carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob, [] { lds_barrier(); });
     const int cs = (ch0 + i) * C;
     const int clen = min(C, sg.s1 - sg.s0 - cs);
     uint16_t* oc = obase + (long)cs * orow;

@@ -100,23 +100,23 @@ def test_workspace_size(g):
         # segment table (varlen) + fp32 start state and bf16 transition per segment and v-head
         return table + a256(segs * hv * dk * dv * 4) + a256(segs * hv * dk * dk * 2)
 
-    # dense bf16: 64 chunks x 32 heads x (Tt, P: 2 x 64 x 64 bf16) + 4 x 64 fp32 scalars; segments of
+    # dense bf16: 64 chunks x 32 heads x (Tt, P: 2 x 64 x 64 bf16) + 8 rows x 64 fp32 scalars; segments of
     # max(8, 64 * 32 / 256) = 8 chunks -> 8 segments
     d = _dims(g)
-    assert g.workspace_size(d) == a256(64 * 32 * 2 * 64 * 64 * 2) + a256(64 * 32 * 4 * 64 * 4) + seg_parts(8)
+    assert g.workspace_size(d) == a256(64 * 32 * 2 * 64 * 64 * 2) + a256(64 * 32 * 8 * 64 * 4) + seg_parts(8)
     # fp32 takes the sequential carry: no segment storage
     d = _dims(g, dtype=g.GDN_F32, chunk_size=32, seqlen=100, num_seqs=3, total_tokens=300)
     units = 3 * 4 * 32
-    assert g.workspace_size(d) == a256(units * 2 * 32 * 32 * 4) + a256(units * 4 * 32 * 4)
+    assert g.workspace_size(d) == a256(units * 2 * 32 * 32 * 4) + a256(units * 8 * 32 * 4)
     # bf16 chunk 16 takes the sequential carry too
     d = _dims(g, chunk_size=16)
     units = 256 * 32
-    assert g.workspace_size(d) == a256(units * 2 * 16 * 16 * 2) + a256(units * 4 * 16 * 4)
+    assert g.workspace_size(d) == a256(units * 2 * 16 * 16 * 2) + a256(units * 8 * 16 * 4)
     # varlen: chunk table + upper bound of chunks; segments bounded by chunks / 8 + sequences
     d = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5)
     chunks = 1000 // 64 + 5
     units = chunks * 32
-    assert g.workspace_size(d) == (256 + a256(units * 2 * 64 * 64 * 2) + a256(units * 4 * 64 * 4)
+    assert g.workspace_size(d) == (256 + a256(units * 2 * 64 * 64 * 2) + a256(units * 8 * 64 * 4)
                                    + seg_parts(chunks // 8 + 5, table=256))
     assert g.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(g, chunk_size=8))) == 0
 
