@@ -268,11 +268,25 @@ def main():
     torch.cuda.synchronize()
     dwall = time.perf_counter() - dw0
     d_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]) * 1e3)
-    d_step = float(np.mean([e[1].elapsed_time(e[2]) for e in devs]) * 1e3)
+    d_step_events = float(np.mean([e[1].elapsed_time(e[2]) for e in devs]) * 1e3)
+    # the recurrent step alone, back to back over the rotating state pools,
+    # with one event pair around the whole run: per-launch average without
+    # the per-call event packets (they add ~3 us to each bracketed call)
+    nrun = args.decode_steps
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    for i in range(nrun):
+        p = i % dinp.pool
+        dec(qd, kd, vd, gs[p], bs[p], pools[i % npool], od)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    d_step = r0.elapsed_time(r1) * 1e3 / nrun
     B_dec = decode_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v)
     dec_gbs = B_dec / (d_step * 1e-6) / 1e9
     decode = {"workload": dinp.name, "batch": Bd, "state_pools": npool, "steps": args.decode_steps,
-              "decode_step_us": round(d_step, 2), "conv_step_us": round(d_conv, 2),
+              "decode_step_us": round(d_step, 2), "decode_step_us_per_call_events": round(d_step_events, 2),
+              "conv_step_us": round(d_conv, 2),
               "ms_per_token_step_wall": round(dwall * 1e3 / args.decode_steps, 4),
               "tokens_per_s": round(Bd / (dwall / args.decode_steps), 1),
               "roofline": {"bound": "hbm", "kernel": "decode_step", "gpu_kernels": CALL_KERNELS["decode_step"],

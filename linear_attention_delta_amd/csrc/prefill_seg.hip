@@ -621,12 +621,12 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
 // outputs, 4..7 stage the chunks and form each chunk's P while the carry
 // works up to its last product, which waits for P at a second barrier.  The staging registers live only
 // in the staging waves, so the carry keeps its accumulators in VGPRs.
-template <int C, int DK, int DV>
-__global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
+template <int C, int DK, int DV, int NCW>
+__global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   typedef SegSmem<C, DK, DV, true> SM;
   constexpr int NDT = DK / 16;
-  constexpr int NCT = DV / 64;  // state column tiles per carry wave
-  static_assert(DV % 64 == 0, "state columns must split over four waves");
+  constexpr int NCT = DV / (16 * NCW);  // state column tiles per carry wave
+  static_assert(NCT * 16 * NCW == DV, "state columns must split over the carry waves");
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = 4 * (lane >> 4);
@@ -638,11 +638,11 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
   const int ch0 = sg.p * a.seg_len;
   const int nch = max(0, min(a.seg_len, nch_seq - ch0));
 
-  if (wave >= 4) {
+  if (wave >= NCW) {
     // staging: chunk i+1 is written to LDS and chunk i+2 requested while
     // the carry waves work on chunk i
     Stager<C, DK, DV, true, 256> st;
-    init_stager(st, a, sg, hk, h, tid - 256);
+    init_stager(st, a, sg, hk, h, tid - 64 * NCW);
     if (nch > 0) {
       st.load(ch0);
       st.store(sm, 0);
@@ -650,7 +650,7 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
     }
     for (int i = 0; i < nch; i++) {
       lds_barrier();
-      compute_p<C, DK, DV, 4>(sm, i & 1, wave - 4, lane);
+      compute_p<C, DK, DV, 4>(sm, i & 1, wave - NCW, lane);
       lds_barrier();  // P ready for the carry's last product
       if (i + 1 < nch) st.store(sm, (i + 1) & 1);
       if (i + 2 < nch) st.load(ch0 + i + 2);
@@ -707,6 +707,8 @@ __global__ void __launch_bounds__(512) k_seg_pass2(ScanArgs a) {
 
 // State-column tiles (16 columns each) per combine workgroup.
 constexpr int kCombineWaves = 1;
+// Carry waves of pass 2 (each owns d_v / (16 kPass2CarryWaves) column tiles).
+constexpr int kPass2CarryWaves = 4;
 
 template <int C, int DK, int DV>
 hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
@@ -723,7 +725,8 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, LW>), dim3(8 * ((units + 7) / 8) * NG), dim3(64 * (CW + LW)), 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_seg_pass2<C, DK, DV>), grid, dim3(512), 0, s, a);
+  constexpr int NCW = kPass2CarryWaves * 16 <= DV ? kPass2CarryWaves : DV / 16;
+  hipLaunchKernelGGL((k_seg_pass2<C, DK, DV, NCW>), grid, dim3(64 * (NCW + 4)), 0, s, a);
   return hipGetLastError();
 }
 
