@@ -170,20 +170,21 @@ def main():
                          head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, seqlen=T, chunk_size=64)
     torch.cuda.synchronize()
 
+    # Two event markers per step: after the conv_prepare call and after the
+    # scan call; a call's duration runs from the previous marker (for the
+    # first step, a marker recorded just before the loop) to its own.
     def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
         cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"])
         if ev is not None:
-            ev[1].record(stream)
+            ev[0].record(stream)
         cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"])
         if ev is not None:
-            ev[2].record(stream)
+            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -195,20 +196,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
-    k_cp = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3   # us
-    k_scan = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    prev = [t_start] + [e[1] for e in evs[:-1]]
+    k_cp = np.array([p.elapsed_time(e[0]) for p, e in zip(prev, evs)]) * 1e3   # us
+    k_scan = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = T / (ms_per_step * 1e-3)
 
     # warm figure: one buffer set, back to back (MALL may serve it)
-    warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
+    warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
     for i in range(10):
         step(sets[0])
+    w0 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
     for i in range(50):
         step(sets[0], warm_evs[i])
     torch.cuda.synchronize()
-    warm_cp = float(np.mean([e[0].elapsed_time(e[1]) for e in warm_evs]) * 1e3)
-    warm_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in warm_evs]) * 1e3)
+    wprev = [w0] + [e[1] for e in warm_evs[:-1]]
+    warm_cp = float(np.mean([p.elapsed_time(e[0]) for p, e in zip(wprev, warm_evs)]) * 1e3)
+    warm_scan = float(np.mean([e[0].elapsed_time(e[1]) for e in warm_evs]) * 1e3)
 
     B_pre = prefill_alg_bytes(T, sh.num_qk_heads, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
     F_pre = prefill_alg_flops(T, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)

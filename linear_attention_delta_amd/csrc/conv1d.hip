@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
 }
 
 constexpr int kConvTok = 8;  // rows per block
-constexpr int kConvRun = 1;  // blocks per thread (longer runs leave the SiLU arithmetic unhidden)
+constexpr int kConvRun = 2;  // blocks per thread: one halo per 16 rows, block 2 loads in flight during block 1
 
 template <class E, int W>
 hipError_t launch_w(const ConvArgs& a, hipStream_t s) {
