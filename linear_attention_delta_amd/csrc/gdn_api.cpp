@@ -34,13 +34,10 @@ gdn_status ok() {
   return GDN_OK;
 }
 
+// Read on every call, so a process can switch the probe on and off.
 bool debug_enabled() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("GDN_DEBUG");
-    v = (e && e[0] == '1') ? 1 : 0;
-  }
-  return v == 1;
+  const char* e = getenv("GDN_DEBUG");
+  return e && e[0] == '1';
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
