@@ -514,13 +514,13 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
 //  - waves 0..CW-1 each own one 16-column tile of S (all rows) in
 //    accumulators, so S feeds the matrix cores straight from registers; they
 //    only store;
-//  - waves CW.. only load: Phi_p and the B_p columns, two steps ahead in two
-//    register sets, into a two-slot LDS ring.
+//  - waves CW.. only load: Phi_p and the B_p columns, NS steps ahead in NS
+//    register sets, into an NS-slot LDS ring.
 // Keeping loads and stores in different waves means no wait for a load ever
 // has to wait for a store to be acknowledged.  The column groups of one
 // v-head get the same blockIdx % 8, i.e. the same XCD, and share its L2 for
 // the transitions.
-template <int DK, int DV, int CW, int LW>
+template <int DK, int DV, int CW, int LW, int NS>
 __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   constexpr int NDT = DK / 16, KS = DK / 32;
   constexpr int NG = DV / (16 * CW);                        // column groups per v-head
@@ -528,8 +528,8 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   constexpr int PV = DK * DK / 8 / LT;                      // 16-byte words of Phi per loader thread
   constexpr int BV = NDT * CW * 64 / LT;                    // f32x4 words of B per loader thread
   static_assert(PV * LT * 8 == DK * DK && BV * LT == NDT * CW * 64, "shape");
-  __shared__ u32x4 phl[2][DK * DK / 8];
-  __shared__ f32x4 bl[2][NDT * CW * 64];                    // [u][tile][lane]
+  __shared__ u32x4 phl[NS][DK * DK / 8];
+  __shared__ f32x4 bl[NS][NDT * CW * 64];                   // [u][tile][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
   const int grp = m8 % NG;                                  // column group
@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
     struct Set {
       u32x4 pf[PV];
       f32x4 bf[BV];
-    } r0, r1;
+    };
     auto load = [&](int p, Set& r) {  // Phi_p and B_p (held in S_start[p+1])
       const u32x4* ph = reinterpret_cast<const u32x4*>(a.seg_phi + ((long)(sbase + p) * a.hv + h) * DK * DK);
 #pragma unroll
@@ -568,20 +568,25 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
     };
     auto put = [&](int p, Set& r) {
 #pragma unroll
-      for (int i = 0; i < PV; i++) phl[p & 1][lt + LT * i] = r.pf[i];
+      for (int i = 0; i < PV; i++) phl[p % NS][lt + LT * i] = r.pf[i];
 #pragma unroll
-      for (int i = 0; i < BV; i++) bl[p & 1][lt + LT * i] = r.bf[i];
+      for (int i = 0; i < BV; i++) bl[p % NS][lt + LT * i] = r.bf[i];
     };
-    load(1, r0);
-    if (last >= 2) load(2, r1);
-    for (int p = 1; p <= last; p += 2) {
-      put(p, r0);
-      if (p + 2 <= last) load(p + 2, r0);
-      lds_barrier();
-      if (p + 1 <= last) {
-        put(p + 1, r1);
-        if (p + 3 <= last) load(p + 3, r1);
-        lds_barrier();
+    // step p's data goes to ring slot p % NS just before barrier p; the
+    // compute waves read it after that barrier
+    Set r[NS];
+#pragma unroll
+    for (int q = 0; q < NS; q++)
+      if (1 + q <= last) load(1 + q, r[q]);
+    for (int p0 = 1; p0 <= last; p0 += NS) {
+#pragma unroll
+      for (int q = 0; q < NS; q++) {
+        const int p = p0 + q;
+        if (p <= last) {
+          put(p, r[q]);
+          if (p + NS <= last) load(p + NS, r[q]);
+          lds_barrier();
+        }
       }
     }
     return;
@@ -596,7 +601,7 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   }
   for (int p = 1; p <= last; p++) {
     lds_barrier();
-    const int b = p & 1;
+    const int b = p % NS;
     f32x4 acc[NDT];
 #pragma unroll
     for (int u = 0; u < NDT; u++) acc[u] = bl[b][(u * CW + wave) * 64 + lane];
@@ -687,7 +692,17 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
 #pragma unroll
     for (int t = 0; t < C / 16; t++) {
       const int tok = 16 * t + c16;
-      if (tok < clen) {
+      if constexpr (NCT == 2) {
+        // lanes g and g^1 (16 apart) trade halves so that each writes 8
+        // adjacent columns: even g the first tile, odd g the second
+        const bool ev = ((lane >> 4) & 1) == 0;
+        const u32x2 send = ev ? ob[1][t] : ob[0][t];
+        const u32x2 recv = {(uint32_t)__shfl_xor((int)send[0], 16, 64), (uint32_t)__shfl_xor((int)send[1], 16, 64)};
+        const u32x4 w = ev ? u32x4{ob[0][t][0], ob[0][t][1], recv[0], recv[1]}
+                           : u32x4{recv[0], recv[1], ob[1][t][0], ob[1][t][1]};
+        const int col = ev ? vcol[0] + r4 : vcol[1] + r4 - 4;
+        if (tok < clen) *reinterpret_cast<u32x4*>(oc + (long)tok * orow + col) = w;
+      } else if (tok < clen) {
 #pragma unroll
         for (int j = 0; j < NCT; j++) *reinterpret_cast<u32x2*>(oc + (long)tok * orow + vcol[j] + r4) = ob[j][t];
       }
@@ -705,8 +720,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   }
 }
 
-// State-column tiles (16 columns each) per combine workgroup.
+// State-column tiles (16 columns each) per combine workgroup, and the depth
+// of its load ring (steps in flight ahead of the chain).
 constexpr int kCombineWaves = 1;
+constexpr int kCombineSlots = 2;
 // Carry waves of pass 2 (each owns d_v / (16 kPass2CarryWaves) column tiles).
 constexpr int kPass2CarryWaves = 4;
 
@@ -722,7 +739,8 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   {
     constexpr int CW = kCombineWaves, LW = 4, NG = DV / (16 * CW);
     const int units = a.num_seqs * a.hv;
-    hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, LW>), dim3(8 * ((units + 7) / 8) * NG), dim3(64 * (CW + LW)), 0, s, a);
+    hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, LW, kCombineSlots>), dim3(8 * ((units + 7) / 8) * NG),
+                       dim3(64 * (CW + LW)), 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   constexpr int NCW = kPass2CarryWaves * 16 <= DV ? kPass2CarryWaves : DV / 16;
