@@ -33,7 +33,10 @@ template <>
 struct Vec<BF16> {
   static constexpr int N = 8;
   typedef u32x4 raw_t;
-  __device__ __forceinline__ static raw_t load_raw(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+  // inputs are read once (the halo rows a second time, from L2): streaming loads
+  __device__ __forceinline__ static raw_t load_raw(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ static void cvt(raw_t w, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -77,17 +80,19 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
   typedef typename E::store_t T;
   constexpr int V = Vec<E>::N;
   constexpr int SPAN = TOK * RUN;  // tokens per thread
-  // One-dimensional grid of (token span, channel block) pairs.  Workgroups
-  // go to the 8 XCDs round-robin by id; each XCD is given one contiguous run
-  // of token spans of a channel block, so the W-1 halo rows a span reads
-  // were fetched into that XCD's L2 by its predecessor.
+  // One-dimensional grid of (token span, channel block) pairs, span-major.
+  // Workgroups go to the 8 XCDs round-robin by id; each XCD is given one
+  // contiguous run of token spans (all channel blocks of each), i.e. one
+  // contiguous stretch of rows, so the W-1 halo rows a span reads were
+  // fetched into that XCD's L2 by its predecessor.
   const int ntb = (a.total_tokens + SPAN - 1) / SPAN;
+  const int ncb = gridDim.x / ntb;  // channel blocks
   int L = blockIdx.x;
   if ((gridDim.x & 7) == 0) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int cg = (L / ntb) * blockDim.x + threadIdx.x;  // channel group
+  const int cg = (L % ncb) * blockDim.x + threadIdx.x;  // channel group
   const int c0 = cg * V;
   if (c0 >= a.channels) return;
-  const int t_begin = (L % ntb) * SPAN;
+  const int t_begin = (L / ncb) * SPAN;
   if (t_begin >= a.total_tokens) return;
   const int t_end = min(t_begin + SPAN, a.total_tokens);
 
