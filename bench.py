@@ -10,8 +10,11 @@ Infinity Cache cannot serve a step from the previous one.
 
 The decode path (conv step + recurrent step, B=64, fp32 32x128x128 states,
 4 rotated state pools of 134 MB) is measured in the same run and reported
-under "decode".  Per-kernel times come from HIP events recorded on the
-launch stream around each library call; each call is one kernel.
+under "decode".  The timed loop runs the steps back to back with no event
+markers in it (a marker leaves the GPU idle for a few microseconds between
+calls).  Per-call times come from HIP events on the launch stream: each
+call alone, run back to back under one event pair (the per-launch time the
+roofline uses), and, separately, a marker after every call of a step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -170,37 +173,62 @@ def main():
                          head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, seqlen=T, chunk_size=64)
     torch.cuda.synchronize()
 
-    # Two event markers per step: after the conv_prepare call and after the
-    # scan call; a call's duration runs from the previous marker (for the
-    # first step, a marker recorded just before the loop) to its own.
-    def step(s, ev=None):
+    def step(s):
         cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"])
-        if ev is not None:
-            ev[0].record(stream)
         cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"])
-        if ev is not None:
-            ev[1].record(stream)
+
+    # Per-call figures: an event marker after each call.  A marker costs the
+    # stream a few microseconds of idle GPU time between the calls, so the
+    # timed loop below runs without any.
+    def step_marked(s, ev):
+        cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"])
+        ev[0].record(stream)
+        cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"])
+        ev[1].record(stream)
+
+    # One call alone, n times back to back over the rotating buffer sets,
+    # with one event pair around the run: its per-launch time.  Every set
+    # holds the same input, so the workspace prepared for one serves all.
+    def back_to_back(fn, n):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for i in range(n):
+            fn(sets[i % nsets])
+        r1.record(stream)
+        torch.cuda.synchronize()
+        return r0.elapsed_time(r1) * 1e3 / n
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(sets[i % nsets], evs[i])
+        step(sets[i % nsets])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
-    prev = [t_start] + [e[1] for e in evs[:-1]]
-    k_cp = np.array([p.elapsed_time(e[0]) for p, e in zip(prev, evs)]) * 1e3   # us
-    k_scan = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = T / (ms_per_step * 1e-3)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    m0 = torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for i in range(args.steps):
+        step_marked(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    prev = [m0] + [e[1] for e in evs[:-1]]
+    k_cp_ev = float(np.mean([p.elapsed_time(e[0]) for p, e in zip(prev, evs)]) * 1e3)   # us
+    k_scan_ev = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+
+    nb = max(args.steps, 20)
+    k_cp = back_to_back(lambda s: cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"]), nb)
+    k_scan = back_to_back(lambda s: cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"]), nb)
 
     # warm figure: one buffer set, back to back (MALL may serve it)
     warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
@@ -209,7 +237,7 @@ def main():
     w0 = torch.cuda.Event(enable_timing=True)
     w0.record(stream)
     for i in range(50):
-        step(sets[0], warm_evs[i])
+        step_marked(sets[0], warm_evs[i])
     torch.cuda.synchronize()
     wprev = [w0] + [e[1] for e in warm_evs[:-1]]
     warm_cp = float(np.mean([p.elapsed_time(e[0]) for p, e in zip(wprev, warm_evs)]) * 1e3)
@@ -218,7 +246,7 @@ def main():
     B_pre = prefill_alg_bytes(T, sh.num_qk_heads, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
     F_pre = prefill_alg_flops(T, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
     B_cp = conv_prepare_alg_bytes(T, CC, sh.num_v_heads)
-    kernels = {"conv_prepare": float(k_cp.mean()), "prefill_scan": float(k_scan.mean())}
+    kernels = {"conv_prepare": float(k_cp), "prefill_scan": float(k_scan)}
     dominant = max(kernels, key=kernels.get)
     dom_us = kernels[dominant]
     dom_bytes = {"conv_prepare": B_cp, "prefill_scan": B_pre}[dominant]
@@ -266,12 +294,15 @@ def main():
     for i in range(20):
         dstep(i)
     torch.cuda.synchronize()
-    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
     dw0 = time.perf_counter()
+    for i in range(args.decode_steps):
+        dstep(i)
+    torch.cuda.synchronize()
+    dwall = time.perf_counter() - dw0
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
     for i in range(args.decode_steps):
         dstep(i, devs[i])
     torch.cuda.synchronize()
-    dwall = time.perf_counter() - dw0
     d_conv = float(np.mean([e[0].elapsed_time(e[1]) for e in devs]) * 1e3)
     d_step_events = float(np.mean([e[1].elapsed_time(e[2]) for e in devs]) * 1e3)
     # the recurrent step alone, back to back over the rotating state pools,
@@ -338,6 +369,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v, 2) for k, v in kernels.items()},
+        "kernels_us_per_call_events": {"conv_prepare": round(k_cp_ev, 2), "prefill_scan": round(k_scan_ev, 2)},
         "gpu_ms_per_step_events": round(gpu_ms / args.steps, 5),
         "step_kernels": {"us": round(step_us, 2), "tokens_per_s": round(T / (step_us * 1e-6), 1),
                          "hbm_frac": round(B_pre / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
