@@ -334,14 +334,17 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
     acc = tile_mma<E, DK>(acc, &sm.u.in.k[16 * j][0], SM::KLD, &sm.u.in.q[16 * i][0], SM::KLD, lane);
     const int r = 16 * i + c16, s0 = 16 * j + r4;
     const float fr = sm.rq[r];
+    const f32x4 rks = *reinterpret_cast<const f32x4*>(&sm.rk[s0]);
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
       const float gr = sm.gam[hh][r];
+      const f32x4 gs = *reinterpret_cast<const f32x4*>(&sm.gam[hh][s0]);
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int s = s0 + e;
-        v[e] = s <= r ? fr * sm.rk[s] * __expf(gr - sm.gam[hh][s]) * acc[e] : 0.f;
+        // computed for every element, then selected (a masked one may be inf)
+        const float val = fr * rks[e] * __expf(gr - gs[e]) * acc[e];
+        v[e] = s0 + e <= r ? val : 0.f;
       }
       T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C;
       if constexpr (std::is_same<E, BF16>::value) {
@@ -389,14 +392,18 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
       tile_ij(t, i, j);
       const int r = 16 * i + c16, s0 = 16 * j + r4;
       const float fr = sm.rk[r];
+      // the four columns' factors as one 16-byte read each, and no branch
+      // per element (a masked element may be inf; the select drops it)
+      const f32x4 rks = *reinterpret_cast<const f32x4*>(&sm.rk[s0]);
 #pragma unroll
       for (int hh = 0; hh < HPW; hh++) {
         const float gr = sm.gam[hh][r], br = sm.bet[hh][r] * fr;
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(&sm.gam[hh][s0]);
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const int s = s0 + e;
-          v[e] = s < r ? br * sm.rk[s] * __expf(gr - sm.gam[hh][s]) * rawA[n][e] : 0.f;
+          const float val = br * rks[e] * __expf(gr - gs[e]) * rawA[n][e];
+          v[e] = s0 + e < r ? val : 0.f;
         }
         *reinterpret_cast<f32x4*>(&sm.u.at[hh][r][s0]) = v;
       }
@@ -459,9 +466,10 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
     for (int idx = tid; idx < C * C / 4; idx += PT) {
       const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0]);
+      const f32x4 bs = *reinterpret_cast<const f32x4*>(&sm.bet[hh][s0]);
       f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * sm.bet[hh][s0 + e] : 0.f;
+      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * bs[e] : 0.f;
       if constexpr (std::is_same<E, BF16>::value) {
         *reinterpret_cast<u32x2*>(out + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
       } else {
