@@ -132,7 +132,7 @@ def main():
                          "scale FETCH_SIZE / WRITE_SIZE by what they read for a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the layer shards by "
               "heads or sequences with no collective inside it); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
