@@ -200,15 +200,31 @@ __device__ __forceinline__ f32x4 ident_c(int lane) {
                4 * g + 3 == c ? 1.f : 0.f};
 }
 
+// Transpose of a 16x16 tile in the accumulator layout through the wave's own
+// 16x16 LDS block at T0 (leading dimension L): written, then read back
+// transposed.  One wave's LDS operations complete in order; the wait and the
+// memory clobber keep the compiler from moving the read above the writes.
+__device__ __forceinline__ f32x4 transpose_lds(float* T0, int L, f32x4 v, int lane) {
+  st_c(T0, L, v, lane);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const f32x4 t = ld_ct(T0, L, lane);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  return t;
+}
+
 // (I + N)^{-1} of a strictly lower 16x16 block N (row-major at A0) by the
 // doubling product (I - N)(I + N^2)(I + N^4)(I + N^8), N^16 = 0.  The
 // factors are polynomials in N and commute, so each step multiplies from the
-// side whose transpose is at hand.
-__device__ __forceinline__ f32x4 inv16(const float* A0, int L, int lane) {
+// side whose transpose is at hand; the transposes of N^2 and N^4 go through
+// the block's own LDS (free once N is in registers) instead of two more
+// products.  The caller writes the inverse back over A0.
+__device__ __forceinline__ f32x4 inv16(float* A0, int L, int lane) {
   const f32x4 id = ident_c(lane);
   const f32x4 n = ld_c(A0, L, lane), nt = ld_ct(A0, L, lane);
-  const f32x4 n2 = mm_tt(nt, n), n2t = mm_tt(n, nt);
-  const f32x4 n4 = mm_tt(n2t, n2), n4t = mm_tt(n2, n2t);
+  const f32x4 n2 = mm_tt(nt, n);
+  const f32x4 n2t = transpose_lds(A0, L, n2, lane);
+  const f32x4 n4 = mm_tt(n2t, n2);
+  const f32x4 n4t = transpose_lds(A0, L, n4, lane);
   const f32x4 n8t = mm_tt(n4, n4t);
   const f32x4 x1 = mm_tt(id - nt, id + n2);   // (I - N)(I + N^2)
   const f32x4 x2 = mm_tt(id + n4t, x1);       // (I + N^4) x1
