@@ -177,8 +177,10 @@ gdn_status gdn_prefill_chunked(const gdn_dims *d, const void *q, const void *k,
  * all state-independent work in batch).  For every chunk and v-head it
  * writes into the workspace Tt = (I + A)^{-1} diag(beta), the causal score
  * matrix P[r][s] = e^{gamma_r - gamma_s} q_hat_r . k_hat_s (s <= r) and the
- * per-token scale factors; fully parallel over chunks.  Arguments as
- * gdn_prefill_chunked.
+ * per-token scale factors; fully parallel over chunks.  For bf16 with chunk
+ * 32 or 64 the carry forms P itself from q and k, so P is not written and
+ * Tt is kept as its nonzero (lower) 16x16 blocks only.  The workspace
+ * layout is private to the library.  Arguments as gdn_prefill_chunked.
  */
 gdn_status gdn_prefill_prepare(const gdn_dims *d, const void *q, const void *k,
                                const float *g, const float *beta,

@@ -475,7 +475,39 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
     }
     lds_barrier();
   }
-  // ---- Tt = inv diag(beta), upper triangle zero, to the workspace
+  // ---- Tt = inv diag(beta), upper triangle zero, to the workspace.  For the
+  // segment-parallel carry only its lower 16x16 blocks are stored, packed:
+  // block n = i(i+1)/2 + j (row tile i, column tile j <= i) is 256 values,
+  // row-major, at 256 n.  The sequential carry reads the full C x C matrix.
+  if constexpr (!WQ) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; hh++) {
+      T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);
+      for (int idx = tid; idx < NT * 32; idx += PT) {  // 8 values (one 16-byte bf16 word) each
+        const int n = idx >> 5, rr = (idx & 31) >> 1, w = idx & 1;
+        int i, j;
+        tile_ij(n, i, j);
+        const int r = 16 * i + rr, s0 = 16 * j + 8 * w;
+        float v[8];
+#pragma unroll
+        for (int h4 = 0; h4 < 2; h4++) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0 + 4 * h4]);
+          const f32x4 bs = *reinterpret_cast<const f32x4*>(&sm.bet[hh][s0 + 4 * h4]);
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[4 * h4 + e] = s0 + 4 * h4 + e <= r ? x[e] * bs[e] : 0.f;
+        }
+        T* dst = out + 256 * n + 16 * rr + 8 * w;
+        if constexpr (std::is_same<E, BF16>::value) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]),
+                                                 cvt_bf16x2(v[4], v[5]), cvt_bf16x2(v[6], v[7])};
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int hh = 0; hh < HPW; hh++) {
     T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);

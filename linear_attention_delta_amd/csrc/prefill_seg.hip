@@ -129,9 +129,13 @@ struct alignas(16) SegSmem {
 template <int C, int DK, int DV, bool OUT, int NTH>
 struct Stager {
   typedef SegSmem<C, DK, DV, OUT> SM;
-  static constexpr int KV = C * DK / 8, VV = C * DV / 8, TV = C * C / 8;  // 16-byte vectors
+  // 16-byte vectors; Tt comes as its NLOW lower 16x16 blocks, packed (block
+  // n = t(t+1)/2 + j, row-major, 32 vectors each)
+  static constexpr int NRT = C / 16, NLOW = NRT * (NRT + 1) / 2;
+  static constexpr int KV = C * DK / 8, VV = C * DV / 8, TV = NLOW * 32;
   static constexpr int NK = (KV + NTH - 1) / NTH, NV = (VV + NTH - 1) / NTH, NT = (TV + NTH - 1) / NTH;
   u32x4 rk[NK], rq[OUT ? NK : 1], rv[NV], rt[NT], rs;
+  int tt_off[NT];  // LDS element offset (row, permuted column) of each Tt vector, the same for every chunk
   const uint16_t *kp, *qp, *vp, *mp;
   const float* sp;
   long sk, sq, sv, mstep, sstep;
@@ -198,14 +202,37 @@ struct Stager {
     }
 #pragma unroll
     for (int j = 0; j < NT; j++) {
-      const int idx = tid + NTH * j, r = idx / (C / 8), lo = perm_lo(idx % (C / 8));
-      if (idx < TV) {
-        *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo]) = u32x2{rt[j][0], rt[j][1]};
-        *reinterpret_cast<u32x2*>(&sm.tt[b][r][lo + 8]) = u32x2{rt[j][2], rt[j][3]};
+      if (TV % NTH == 0 || tid + NTH * j < TV) {
+        uint16_t* d = &sm.tt[b][0][0] + tt_off[j];
+        *reinterpret_cast<u32x2*>(d) = u32x2{rt[j][0], rt[j][1]};
+        *reinterpret_cast<u32x2*>(d + 8) = u32x2{rt[j][2], rt[j][3]};
       }
     }
     // row 6 is this stager's own (scale rq, above)
     if (tid < (OUT ? 2 : 1) * C && (4 * tid) / C != 6) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + 4 * tid) = rs;
+  }
+
+  // Where each of this thread's packed Tt vectors goes in a chunk buffer
+  // (vector idx: block n = idx / 32, its row (idx % 32) / 2, half idx % 2),
+  // and zeros in the upper blocks (t, t + 1), t even, of both buffers: the
+  // carry's 32-wide k steps read them, the workspace does not hold them and
+  // no chunk's store touches them.  Once, before the first store.
+  __device__ __forceinline__ void setup_tt(SM& sm) {
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+      const int idx = tid + NTH * j;
+      const int n = idx < TV ? idx >> 5 : 0, rr = (idx & 31) >> 1, w = idx & 1;
+      int t = 0;
+      while ((t + 1) * (t + 2) / 2 <= n) t++;
+      tt_off[j] = (16 * t + rr) * SM::CLD + perm_lo(2 * (n - t * (t + 1) / 2) + w);
+    }
+    constexpr int NZW = 2 * (NRT / 2) * 32;  // (buffer, block, row, half)
+    for (int idx = tid; idx < NZW; idx += NTH) {
+      const int w = idx & 1, rr = (idx >> 1) & 15, z = (idx >> 5) % (NRT / 2), b = idx / (NRT / 2 * 32);
+      const int t = 2 * z, lo = perm_lo(2 * (t + 1) + w);
+      *reinterpret_cast<u32x2*>(&sm.tt[b][16 * t + rr][lo]) = u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(&sm.tt[b][16 * t + rr][lo + 8]) = u32x2{0u, 0u};
+    }
   }
 };
 
@@ -458,6 +485,7 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
   Stager<C, DK, DV, false, 64 * NW> st;
   init_stager(st, a, sg, hk, h, tid);
   st.load(ch0);
+  st.setup_tt(sm);
   st.store(sm, 0);
   if (nch > 1) st.load(ch0 + 1);
   u32x2 ob[NCT][C / 16];
@@ -650,6 +678,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
     init_stager(st, a, sg, hk, h, tid - 64 * NCW);
     if (nch > 0) {
       st.load(ch0);
+      st.setup_tt(sm);
       st.store(sm, 0);
       if (nch > 1) st.load(ch0 + 1);
     }
