@@ -136,29 +136,48 @@ struct Stager {
   static constexpr int NK = (KV + NTH - 1) / NTH, NV = (VV + NTH - 1) / NTH, NT = (TV + NTH - 1) / NTH;
   u32x4 rk[NK], rq[OUT ? NK : 1], rv[NV], rt[NT], rs;
   int tt_off[NT];  // LDS element offset (row, permuted column) of each Tt vector, the same for every chunk
+  // this thread's K, Q and V vectors: row within the chunk (C, never loaded,
+  // past the arrays) and element offset from the chunk's first row, the same
+  // for every chunk
+  int krow[NK], vrow[NV];
+  long koff[NK], qoff[OUT ? NK : 1], voff[NV];
   const uint16_t *kp, *qp, *vp, *mp;
   const float* sp;
   long sk, sq, sv, mstep, sstep;
   int ntok, tid, l2norm;
   float scale;
 
-  __device__ __forceinline__ void load(int ch) {  // ch: chunk index within the sequence
-    const int cs = ch * C;
-    const int clen = min(C, ntok - cs);
+  __device__ __forceinline__ void setup_offsets() {
 #pragma unroll
     for (int j = 0; j < NK; j++) {
       const int idx = tid + NTH * j, r = idx / (DK / 8), cv = idx % (DK / 8);
-      const bool ok = idx < KV && r < clen;
-      rk[j] = ok ? *reinterpret_cast<const u32x4*>(kp + (long)(cs + r) * sk + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (OUT)
-        rq[j] = ok ? *reinterpret_cast<const u32x4*>(qp + (long)(cs + r) * sq + 8 * cv) : u32x4{0u, 0u, 0u, 0u};
+      krow[j] = idx < KV ? r : C;
+      koff[j] = (long)r * sk + 8 * cv;
+      if constexpr (OUT) qoff[j] = (long)r * sq + 8 * cv;
     }
 #pragma unroll
     for (int j = 0; j < NV; j++) {
       const int idx = tid + NTH * j, r = idx / (DV / 8), cv = idx % (DV / 8);
-      rv[j] = (idx < VV && r < clen) ? *reinterpret_cast<const u32x4*>(vp + (long)(cs + r) * sv + 8 * cv)
-                                     : u32x4{0u, 0u, 0u, 0u};
+      vrow[j] = idx < VV ? r : C;
+      voff[j] = (long)r * sv + 8 * cv;
     }
+  }
+
+  __device__ __forceinline__ void load(int ch) {  // ch: chunk index within the sequence
+    const int cs = ch * C;
+    const int clen = min(C, ntok - cs);
+    const uint16_t* kc = kp + (long)cs * sk;
+    const uint16_t* qc = qp + (long)cs * sq;
+    const uint16_t* vc = vp + (long)cs * sv;
+#pragma unroll
+    for (int j = 0; j < NK; j++) {
+      const bool ok = krow[j] < clen;
+      rk[j] = ok ? *reinterpret_cast<const u32x4*>(kc + koff[j]) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (OUT) rq[j] = ok ? *reinterpret_cast<const u32x4*>(qc + qoff[j]) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < NV; j++)
+      rv[j] = vrow[j] < clen ? *reinterpret_cast<const u32x4*>(vc + voff[j]) : u32x4{0u, 0u, 0u, 0u};
     const uint16_t* mc = mp + ch * mstep;
 #pragma unroll
     for (int j = 0; j < NT; j++) {
@@ -439,6 +458,7 @@ __device__ __forceinline__ void init_stager(Stager<C, DK, DV, OUT, NTH>& st, con
   st.sstep = (long)a.hv * (kScalRows * C);
   st.l2norm = a.l2norm;
   st.scale = a.scale;
+  st.setup_offsets();
 }
 
 // ------------------------------------------------------------------ pass 1
