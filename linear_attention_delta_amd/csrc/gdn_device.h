@@ -43,6 +43,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
+// c + a.lo b.lo + a.hi b.hi for two packed bf16 pairs, in fp32, one
+// instruction (sums of squares for the q/k norms).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // Two fp32 -> packed bf16 pair with the gfx950 convert instruction (round to
 // nearest even).  Used on the tolerance-checked paths; the bit-exact
 // convolution keeps its own rounding above.

@@ -300,12 +300,17 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
       if (idx < KQV) *reinterpret_cast<u32x4*>(which ? &sm.u.in.q[r][cv * EPV] : &sm.u.in.k[r][cv * EPV]) = w[j];
-      const T* e = reinterpret_cast<const T*>(&w[j]);
       float ss = 0.f;
+      if constexpr (std::is_same<E, BF16>::value) {
 #pragma unroll
-      for (int i = 0; i < EPV; i++) {
-        const float x = E::to_f32(e[i]);
-        ss += x * x;
+        for (int i = 0; i < 4; i++) ss = dot2_bf16(w[j][i], w[j][i], ss);
+      } else {
+        const T* e = reinterpret_cast<const T*>(&w[j]);
+#pragma unroll
+        for (int i = 0; i < EPV; i++) {
+          const float x = E::to_f32(e[i]);
+          ss += x * x;
+        }
       }
       ss = group_sum<VPR>(ss);
       if (cv == 0 && idx < KQV) {

@@ -204,11 +204,7 @@ struct Stager {
         // scale / |q_r| (row 6): the DK/8 words of a row sit in consecutive lanes
         float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float x0 = __uint_as_float(rq[j][e] << 16), x1 = __uint_as_float(rq[j][e] & 0xffff0000u);
-          ss += x0 * x0;
-          ss += x1 * x1;
-        }
+        for (int e = 0; e < 4; e++) ss = dot2_bf16(rq[j][e], rq[j][e], ss);
         ss = group_sum<DK / 8>(ss);
         if (idx < KV && idx % (DK / 8) == 0)
           sm.sc[b][6][r] = scale * (l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f);
