@@ -10,7 +10,7 @@ Infinity Cache cannot serve a step from the previous one.
 
 The decode path (conv step + recurrent step, B=64, fp32 32x128x128 states,
 4 rotated state pools of 134 MB) is measured in the same run and reported
-under "decode".  The timed loop runs the steps back to back with no event
+under "decode", as two library calls and as the one fused call.  The timed loop runs the steps back to back with no event
 markers in it (a marker leaves the GPU idle for a few microseconds between
 calls).  Per-call times come from HIP events on the launch stream: each
 call alone, run back to back under one event pair (the per-launch time the
@@ -64,16 +64,24 @@ def decode_alg_bytes(B, hk, hv, dk, dv, esize=2):
     return 2 * B * hv * dk * dv * 4 + B * (2 * hk * dk + 2 * hv * dv) * esize + 2 * B * hv * 4
 
 
+def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
+    """The fused step: state read and written, the raw row and the conv
+    window (read and written) in, o out, g and beta, and the conv taps."""
+    cc = 2 * hk * dk + hv * dv
+    return (2 * B * hv * dk * dv * 4 + B * cc * esize + 2 * B * (W - 1) * cc * esize + B * hv * dv * esize
+            + 2 * B * hv * 4 + cc * W * 4)
+
+
 KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
-                  "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip"],
-                  "conv_step": ["conv1d.hip", "conv_math.h"]}
+                  "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip", "conv_math.h"],
+                  "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"]}
 # The GPU kernels each library call launches on the 4096-token bf16 layer
 # (conv_prepare: the convolution, then the chunk prepare; the scan call runs
 # the segment-parallel carry: two passes and a combine) and on the
-# 64-sequence decode step.
+# 64-sequence decode step (two calls, or the one fused call).
 CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
                 "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
-                "conv_step": ["k_conv_step"]}
+                "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"]}
 
 
 def source_digest(kernel=None):
@@ -320,6 +328,34 @@ def main():
     d_step = r0.elapsed_time(r1) * 1e3 / nrun
     B_dec = decode_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v)
     dec_gbs = B_dec / (d_step * 1e-6) / 1e9
+
+    # the same step as one fused call (conv step + recurrent step in one
+    # kernel): wall time of the marker-free loop, and the per-launch time
+    # back to back under one event pair
+    fused = gdn.DecodeConv(xs[0], wd, num_qk_heads=dsh.num_qk_heads, num_v_heads=dsh.num_v_heads,
+                           head_dim_k=dsh.head_dim_k, head_dim_v=dsh.head_dim_v, num_slots=Bd)
+
+    def fstep(i):
+        p = i % dinp.pool
+        fused(xs[p], gs[p], bs[p], pools[i % npool], cwins[i % npool], od)
+
+    for i in range(20):
+        fstep(i)
+    torch.cuda.synchronize()
+    fw0 = time.perf_counter()
+    for i in range(args.decode_steps):
+        fstep(i)
+    torch.cuda.synchronize()
+    fwall = time.perf_counter() - fw0
+    r0.record(stream)
+    for i in range(nrun):
+        fstep(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    f_step = r0.elapsed_time(r1) * 1e3 / nrun
+    B_fused = decode_conv_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v,
+                                    W=dinp.conv_w.shape[1])
+    fused_gbs = B_fused / (f_step * 1e-6) / 1e9
     decode = {"workload": dinp.name, "batch": Bd, "state_pools": npool, "steps": args.decode_steps,
               "decode_step_us": round(d_step, 2), "decode_step_us_per_call_events": round(d_step_events, 2),
               "conv_step_us": round(d_conv, 2),
@@ -329,7 +365,16 @@ def main():
                            "achieved": round(dec_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                            "traffic": read_traffic("decode_step", dinp.name), "alg_bytes_per_launch": int(B_dec),
-                           "avg_launch_us": round(d_step, 2)}}
+                           "avg_launch_us": round(d_step, 2)},
+              "fused_conv_step": {
+                  "decode_conv_step_us": round(f_step, 2),
+                  "ms_per_token_step_wall": round(fwall * 1e3 / args.decode_steps, 4),
+                  "tokens_per_s": round(Bd / (fwall / args.decode_steps), 1),
+                  "roofline": {"bound": "hbm", "kernel": "decode_conv_step",
+                               "gpu_kernels": CALL_KERNELS["decode_conv_step"], "achieved": round(fused_gbs, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+                               "traffic": read_traffic("decode_conv_step", dinp.name),
+                               "alg_bytes_per_launch": int(B_fused), "avg_launch_us": round(f_step, 2)}}}
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None

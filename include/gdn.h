@@ -263,6 +263,42 @@ gdn_status gdn_decode_step(const gdn_dims *d, const void *q, const void *k,
                            float *state, int32_t num_slots,
                            const int32_t *state_slots, void *o, void *stream);
 
+/*
+ * One decode step from the raw projected row: the layer's short causal
+ * conv1d + SiLU (Vallmo.jl README, "What's here") for the new token, its
+ * window kept per sequence as the oxydllm notes ("New Features") keep it,
+ * fused with the recurrent step of gdn_decode_step on the q, k, v it
+ * produces, which never go through memory.  The result (o, state and the
+ * windows) equals, bit for bit,
+ *     gdn_conv1d(B, B, 1, NULL, C_conv, conv_width, dtype, x, stride_x,
+ *                conv_weight, conv_bias, W_b, 1, y, C_conv)
+ *     gdn_decode_step(d, y, y + H_k d_k, y + 2 H_k d_k, g, beta, state, ...)
+ * where W_b holds, in sequence order, the windows of the sequences' slots
+ * (d's token strides set to C_conv).
+ *
+ * d: as gdn_decode_step, with at most 4 v-heads per q/k head
+ * (GDN_ERR_UNSUPPORTED otherwise: one workgroup convolves a q/k head once
+ * for all its v-heads); its stride_q, stride_k and stride_v are not used
+ * (0 or any value gdn_validate_dims accepts).  x: [B] rows of C_conv =
+ * 2 H_k d_k + H_v d_v channels ordered [q | k | v], token stride stride_x
+ * (>= C_conv, a multiple of 16 bytes), 16-byte aligned.  conv_width: W in
+ * [2, 8]; conv_weight fp32 [C_conv][W]; conv_bias fp32 [C_conv] or NULL.
+ * conv_state: [num_slots][W-1][C_conv] in dtype, required, 16-byte aligned,
+ * not overlapping x: sequence b reads and advances the window of slot
+ * state_slots[b] (or b), the same slot as its recurrent state.  g, beta,
+ * state, num_slots, state_slots, o: as gdn_decode_step (two sequences must
+ * not share a slot; a slot outside [0, num_slots) gives NaN outputs for that
+ * sequence and leaves its state and window alone).
+ */
+gdn_status gdn_decode_conv_step(const gdn_dims *d, int32_t conv_width,
+                                const void *x, int64_t stride_x,
+                                const float *conv_weight,
+                                const float *conv_bias, void *conv_state,
+                                const float *g, const float *beta,
+                                float *state, int32_t num_slots,
+                                const int32_t *state_slots, void *o,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

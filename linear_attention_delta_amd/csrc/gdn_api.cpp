@@ -532,4 +532,71 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
   return ok();
 }
 
+gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+                                const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
+                                const float* beta, float* state, int32_t num_slots, const int32_t* state_slots,
+                                void* o, void* stream) {
+  gdn_status st = check_dims(d, 1);
+  if (st != GDN_OK) return st;
+  const int64_t cc = 2LL * d->num_qk_heads * d->head_dim_k + (int64_t)d->num_v_heads * d->head_dim_v;
+  const int vec = d->dtype == GDN_BF16 ? 8 : 4;
+  const size_t esz = elem_size(d->dtype);
+  if (conv_width < 2 || conv_width > 8) return fail(GDN_ERR_UNSUPPORTED, "conv_width must be in [2, 8] (got %d)", conv_width);
+  if (d->num_v_heads / d->num_qk_heads > 4)
+    return fail(GDN_ERR_UNSUPPORTED, "the fused step takes at most 4 v-heads per q/k head (got %d)",
+                d->num_v_heads / d->num_qk_heads);
+  if (stride_x < cc || stride_x % vec)
+    return fail(GDN_ERR_INVALID_ARG, "stride_x must be >= %lld channels and a multiple of %d", (long long)cc, vec);
+  if (!x || !aligned(x, 16)) return fail(GDN_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
+  if (!conv_weight || !aligned(conv_weight, 4))
+    return fail(GDN_ERR_INVALID_ARG, "conv_weight must be non-NULL and 4-byte aligned");
+  if (conv_bias && !aligned(conv_bias, 4)) return fail(GDN_ERR_INVALID_ARG, "conv_bias must be 4-byte aligned");
+  if (!conv_state || !aligned(conv_state, 16))
+    return fail(GDN_ERR_INVALID_ARG, "conv_state must be non-NULL and 16-byte aligned");
+  if (!g || !beta || !aligned(g, 4) || !aligned(beta, 4))
+    return fail(GDN_ERR_INVALID_ARG, "g and beta must be non-NULL and 4-byte aligned");
+  if (!o || !aligned(o, 16)) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
+  if (!state || !aligned(state, 16)) return fail(GDN_ERR_INVALID_ARG, "state must be non-NULL and 16-byte aligned");
+  if (num_slots < 1) return fail(GDN_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (!state_slots && num_slots < d->num_seqs)
+    return fail(GDN_ERR_INVALID_ARG, "without state_slots, num_slots (%d) must be >= num_seqs (%d)", num_slots,
+                d->num_seqs);
+  if (state_slots && !aligned(state_slots, 4)) return fail(GDN_ERR_INVALID_ARG, "state_slots must be 4-byte aligned");
+  {
+    const char* x0 = reinterpret_cast<const char*>(x);
+    const char* w0 = reinterpret_cast<const char*>(conv_state);
+    const size_t xb = ((size_t)(d->num_seqs - 1) * stride_x + cc) * esz;
+    const size_t wb = (size_t)num_slots * (conv_width - 1) * cc * esz;
+    if (x0 < w0 + wb && w0 < x0 + xb) return fail(GDN_ERR_INVALID_ARG, "x and conv_state must not overlap");
+  }
+  gdn::ConvArgs c;
+  c.num_seqs = d->num_seqs;
+  c.total_tokens = d->num_seqs;
+  c.seqlen = 1;
+  c.cu_seqlens = nullptr;
+  c.channels = (int)cc;
+  c.width = conv_width;
+  c.dtype = d->dtype;
+  c.activation = 1;
+  c.x = x;
+  c.stride_x = stride_x;
+  c.weight = conv_weight;
+  c.bias = conv_bias;
+  c.conv_state = conv_state;
+  c.y = nullptr;
+  c.stride_y = 0;
+  gdn::ScanArgs a = make_args(d);
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.state = state;
+  a.state_slots = state_slots;
+  a.num_slots = num_slots;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_decode_conv(a, c, s);
+  if (e != hipSuccess) return hip_fail(e, "decode conv launch");
+  if ((st = debug_check(s, "o", o, (long)d->num_seqs * d->num_v_heads * d->head_dim_v, d->dtype)) != GDN_OK) return st;
+  return ok();
+}
+
 }  // extern "C"

@@ -73,6 +73,9 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 bool seg_path(const ScanArgs& a);
 hipError_t launch_seg(const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(const ScanArgs& a, hipStream_t s);
+// decode step with the conv step fused in (c.x, c.stride_x, c.weight, c.bias,
+// c.conv_state, c.channels and c.width are used; the window is per slot)
+hipError_t launch_decode_conv(const ScanArgs& a, const ConvArgs& c, hipStream_t s);
 // GDN_DEBUG: count non-finite values (fp32 or bf16) into *count (device int).
 hipError_t launch_nonfinite_probe(const void* p, long n, int dtype, int* count, hipStream_t s);
 

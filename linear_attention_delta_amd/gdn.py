@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
-            "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step"]
+            "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step"]
 
 
 class GdnDims(ctypes.Structure):
@@ -67,6 +67,7 @@ def _load():
         "gdn_prefill_conv_prepare": ([D, i32, P, i64, P, P, P, P, P, P, P, i64, P, sz, P], i32),
         "gdn_prefill_conv_chunked": ([D, i32, P, i64, P, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
+        "gdn_decode_conv_step": ([D, i32, P, i64, P, P, P, P, P, P, i32, P, P, P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -352,4 +353,53 @@ def decode_step(q, k, v, g, beta, state, *, state_slots=None, l2norm=True, heads
         out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
     _check(lib.gdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                state.shape[0], _ptr(state_slots), _ptr(out), _stream(stream)))
+    return out
+
+
+def _decode_conv_dims(x, *, num_qk_heads, num_v_heads, head_dim_k, head_dim_v, l2norm, heads_tiled, scale):
+    B, cc = x.shape
+    if cc != 2 * num_qk_heads * head_dim_k + num_v_heads * head_dim_v:
+        raise ValueError("x must have 2 H_k d_k + H_v d_v channels")
+    return make_dims(num_seqs=B, total_tokens=B, seqlen=1, num_qk_heads=num_qk_heads, num_v_heads=num_v_heads,
+                     head_dim_k=head_dim_k, head_dim_v=head_dim_v, chunk_size=64, dtype=_dtype_code(x),
+                     l2norm=l2norm, heads_tiled=heads_tiled, scale=scale)
+
+
+class DecodeConv:
+    """Bound decode step from raw rows x [B, C_conv] (channels [q | k | v],
+    rows may be strided): conv step + SiLU and the recurrent step in one
+    library call.  Sizes, conv weights and stream fixed at construction."""
+
+    def __init__(self, x, weight, *, num_qk_heads, num_v_heads, head_dim_k, head_dim_v, num_slots, bias=None,
+                 l2norm=True, heads_tiled=False, scale=1.0, stream=None):
+        self.dims = _decode_conv_dims(x, num_qk_heads=num_qk_heads, num_v_heads=num_v_heads,
+                                      head_dim_k=head_dim_k, head_dim_v=head_dim_v, l2norm=l2norm,
+                                      heads_tiled=heads_tiled, scale=scale)
+        self._d = ctypes.byref(self.dims)
+        self.width = weight.shape[1]
+        self._w = (_ptr(weight), _ptr(bias))
+        self._keep = (weight, bias)
+        self.num_slots = int(num_slots)
+        self._stream = _stream(stream)
+
+    def __call__(self, x, g, beta, state, conv_state, out, state_slots=None):
+        _check(lib.gdn_decode_conv_step(self._d, self.width, x.data_ptr(), x.stride(0), *self._w,
+                                        conv_state.data_ptr(), g.data_ptr(), beta.data_ptr(), state.data_ptr(),
+                                        self.num_slots, _ptr(state_slots), out.data_ptr(), self._stream))
+        return out
+
+
+def decode_conv_step(x, weight, g, beta, state, conv_state, *, num_qk_heads, num_v_heads, head_dim_k, head_dim_v,
+                     bias=None, state_slots=None, l2norm=True, heads_tiled=False, scale=1.0, out=None, stream=None):
+    """One token per sequence from raw rows x [B, 2 H_k d_k + H_v d_v]; weight
+    fp32 [C_conv, W]; conv_state [slots, W-1, C_conv] and state fp32
+    [slots, H_v, d_k, d_v] are advanced in place.  Returns o [B, H_v, d_v]."""
+    import torch
+    d = _decode_conv_dims(x, num_qk_heads=num_qk_heads, num_v_heads=num_v_heads, head_dim_k=head_dim_k,
+                          head_dim_v=head_dim_v, l2norm=l2norm, heads_tiled=heads_tiled, scale=scale)
+    if out is None:
+        out = torch.empty((x.shape[0], num_v_heads, head_dim_v), dtype=x.dtype, device=x.device)
+    _check(lib.gdn_decode_conv_step(ctypes.byref(d), weight.shape[1], _ptr(x), x.stride(0), _ptr(weight), _ptr(bias),
+                                    _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), state.shape[0],
+                                    _ptr(state_slots), _ptr(out), _stream(stream)))
     return out

@@ -172,3 +172,29 @@ def test_conv_entry_points_reject_before_any_gpu_call(g):
                                       None, 256, ws, None) == 1
     assert L.gdn_prefill_conv_chunked(ctypes.byref(d), 4, X, cc, W, None, None, GG, B, 8, None, Y, cc, 1 << 43,
                                       None, 256, ws, None) == 1  # misaligned state_in
+
+
+def test_decode_conv_step_rejects_before_any_gpu_call(g):
+    """The fused decode step validates everything on the host."""
+    L = g.lib
+    cc = 8192
+    d = _dims(g, num_seqs=4, total_tokens=4, seqlen=1)
+    X, CS, W, GG, B, S, O = (1 << 32, 1 << 36, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44)  # fake, disjoint
+
+    def step(dd=d, width=4, x=X, sx=cc, w=W, cs=CS, st=S, slots=4, o=O):
+        return L.gdn_decode_conv_step(ctypes.byref(dd), width, x, sx, w, None, cs, GG, B, st, slots, None, o, None)
+
+    assert step(dd=_dims(g)) == 1                  # not a decode problem (seqlen != 1)
+    assert step(width=9) == 2 and step(width=1) == 2
+    assert step(sx=cc - 8) == 1                    # stride below the channel count
+    assert step(sx=cc + 4) == 1                    # stride not a multiple of 8 bf16
+    assert step(x=X + 2) == 1                      # misaligned x
+    assert step(w=0) == 1                          # no weight
+    assert step(cs=0) == 1                         # the window is required
+    assert step(cs=X + 2 * cc * 2) == 1            # window overlaps x
+    assert step(st=0) == 1                         # no state
+    assert step(o=0) == 1                          # no output
+    assert step(slots=2) == 1                      # fewer slots than sequences without a slot map
+    assert L.gdn_decode_conv_step(ctypes.byref(d), 4, X, cc, W, None, CS, 0, B, S, 4, None, O, None) == 1  # no g
+    d8 = _dims(g, num_seqs=4, total_tokens=4, seqlen=1, num_qk_heads=4, num_v_heads=32)
+    assert step(dd=d8, sx=2 * 4 * 128 + 32 * 128) == 2   # 8 v-heads per q/k head: not supported fused

@@ -36,6 +36,11 @@ def test_conv_prepare_and_decode_bytes():
     assert bench.conv_prepare_alg_bytes(4096, 8192, 32) == 135_397_376
     # state read + written once, plus the token's q, k, v, o, g, beta
     assert bench.decode_alg_bytes(64, 16, 32, 128, 128) == 270_024_704
+    # fused: state read + written, the raw 8192-channel row, the 3-row window
+    # read + written, o, g, beta and the 8192 x 4 fp32 taps
+    fused = 2 * 64 * 32 * 128 * 128 * 4 + 64 * 8192 * 2 + 2 * 64 * 3 * 8192 * 2 + 64 * 32 * 128 * 2 \
+        + 2 * 64 * 32 * 4 + 8192 * 4 * 4
+    assert bench.decode_conv_alg_bytes(64, 16, 32, 128, 128, W=4) == fused == 276_447_232
 
 
 def test_call_kernels_exist_in_their_sources():
