@@ -52,6 +52,8 @@ class Oracle:
         lib.gdn_oracle_scan.argtypes = [i32, P, i32, i32, i32, i32, ctypes.c_double, ctypes.c_uint,
                                         P, P, P, P, P, P, P, P, i32]
         lib.gdn_oracle_scan.restype = i32
+        lib.gdn_oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i32, P, P, P, ctypes.c_double, P]
+        lib.gdn_oracle_gated_rmsnorm.restype = None
         lib.gdn_oracle_available_cores.argtypes = []
         lib.gdn_oracle_available_cores.restype = i32
         self.lib = lib
@@ -125,6 +127,16 @@ class Oracle:
             raise ValueError("oracle scan rejected the shapes")
         return (o, S, nt) if return_threads else (o, S)
 
+    def gated_rmsnorm(self, o, z, w, *, eps=1e-6):
+        """Gated RMS norm in fp64: o, z [..., d] (the last axis is one v-head's
+        values), w [d].  Returns y of o's shape."""
+        o, z, w = _f64(o), _f64(z), _f64(w)
+        assert o.shape == z.shape and w.shape == (o.shape[-1],)
+        d = o.shape[-1]
+        y = np.zeros(o.shape, dtype=np.float64)
+        self.lib.gdn_oracle_gated_rmsnorm(o.size // d if d else 0, d, _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y))
+        return y
+
     def decode_step(self, q, k, v, g, beta, state, *, scale=1.0, l2norm=True, heads_tiled=False,
                     n_threads=0):
         """One recurrent step for B sequences (one token each): q, k [B][H_k][d_k],
@@ -184,6 +196,10 @@ def scan(*a, **kw):
 
 def decode_step(*a, **kw):
     return default().decode_step(*a, **kw)
+
+
+def gated_rmsnorm(*a, **kw):
+    return default().gated_rmsnorm(*a, **kw)
 
 
 def source_text() -> str:

@@ -49,6 +49,16 @@
  *
  * The decode step is this scan with one token per sequence.
  *
+ *  - gdn_oracle_gated_rmsnorm: the gated RMS norm applied to the layer's
+ *    output before the output projection (the oxydllm notes, "Performance":
+ *    the Gated DeltaNet's gated norm runs as one fused kernel over the token
+ *    batch; "New Features", GGUF qwen35: this norm, unlike the model's other
+ *    norms, uses its weight as stored, with no plus-one).  Per (token,
+ *    v-head) row of d_v values, with gate z and weight w[d_v] shared by all
+ *    heads:
+ *        y_j = w_j * o_j / sqrt(mean_i o_i^2 + eps) * silu(z_j),
+ *    silu(a) = a / (1 + e^-a): normalise first, then gate.
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread -lm.
  * -ffp-contract=off matters: the fp32 convolution must not gain or lose
  * fused multiply-adds behind the source's back.
@@ -299,4 +309,19 @@ int gdn_oracle_scan(int n_seq, const int32_t *cu, int Hk, int Hv, int dk, int dv
     for (int i = 0; i < nt; i++) pthread_join(th[i], NULL);
     free(th);
     return nt;
+}
+
+/* ---------------------------------------------------------- gated norm */
+
+/* o, z, y: [rows][d] (a row is one token's one v-head); w: [d]. */
+void gdn_oracle_gated_rmsnorm(long rows, int d, const double *o, const double *z,
+                              const double *w, double eps, double *y)
+{
+    for (long r = 0; r < rows; r++) {
+        const double *orow = o + r * d, *zrow = z + r * d;
+        double ss = 0.0;
+        for (int j = 0; j < d; j++) ss += orow[j] * orow[j];
+        const double inv_rms = 1.0 / sqrt(ss / d + eps);
+        for (int j = 0; j < d; j++) y[r * d + j] = w[j] * orow[j] * inv_rms * silu_f64(zrow[j]);
+    }
 }

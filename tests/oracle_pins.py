@@ -431,5 +431,66 @@ def pin_conv_f32(orc):
     assert orc.exp_f32(0.0) == 1.0 and orc.exp_f32(100.0) == math.inf and orc.exp_f32(-100.0) == 0.0
 
 
+# --------------------------------------------------------------- gated norm
+# y_j = w_j o_j / sqrt(mean(o^2) + eps) silu(z_j) per (token, v-head) row.
+
+def _silu(a):
+    return a * expit(a)
+
+
+def pin_gated_norm_closed_forms(orc):
+    """Rows whose root mean square is known by hand."""
+    d = 4
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    g = 0.75 * math.log(3.0)                 # silu(ln 3) = ln 3 / (1 + 1/3)
+    z = np.full((1, d), math.log(3.0))
+    # [3, 4, 0, 0]: mean square 25/4, rms 2.5 (eps 0)
+    y = orc.gated_rmsnorm(np.array([[3.0, 4.0, 0.0, 0.0]]), z, w, eps=0.0)
+    _close(y, [[1.2 * g, 3.2 * g, 0.0, 0.0]], 1e-14, what="[3,4,0,0] row")
+    # a constant row c: o / rms = c / sqrt(c^2 + eps), weight and gate by element
+    c, eps = 0.37, 1e-6
+    y = orc.gated_rmsnorm(np.full((1, d), c), z, w, eps=eps)
+    _close(y, [w * c / math.sqrt(c * c + eps) * g], 1e-14, what="constant row")
+    # a tiny row, where eps decides the scale: delta / sqrt(delta^2 + eps)
+    dl = 1e-5
+    y = orc.gated_rmsnorm(np.full((1, d), -dl), np.full((1, d), 2.0), w, eps=eps)
+    _close(y, [-w * dl / math.sqrt(dl * dl + eps) * (2.0 / (1.0 + math.exp(-2.0)))], 1e-13, what="eps-dominated row")
+
+
+def pin_gated_norm_gate(orc):
+    """The gate: z = 0 gives 0; silu(z) - silu(-z) = z, so y(z) - y(-z) is the
+    normalised, weighted row times z."""
+    r = _rng(40)
+    rows, d = 5, 16
+    o = r.normal(size=(rows, d))
+    z = r.normal(size=(rows, d)) * 3
+    w = r.normal(size=d)
+    assert np.all(orc.gated_rmsnorm(o, np.zeros_like(z), w) == 0.0)
+    diff = orc.gated_rmsnorm(o, z, w) - orc.gated_rmsnorm(o, -z, w)
+    rms = np.sqrt(np.mean(o * o, axis=1, keepdims=True) + EPS)
+    _close(diff, w * o / rms * z, 1e-12, what="odd part of the gate")
+
+
+def pin_gated_norm_rows_independent(orc):
+    """Each (token, v-head) row is normalised on its own: changing one row
+    changes no other, and with eps = 0 scaling a row by l > 0 leaves it
+    unchanged."""
+    r = _rng(41)
+    T, H, d = 3, 4, 8
+    o = r.normal(size=(T, H, d))
+    z = r.normal(size=(T, H, d))
+    w = r.normal(size=d)
+    y0 = orc.gated_rmsnorm(o, z, w)
+    o2 = o.copy()
+    o2[1, 2] *= 7.0
+    o2[2, 0] += 1.0
+    y1 = orc.gated_rmsnorm(o2, z, w)
+    changed = np.any(y1 != y0, axis=-1)
+    assert changed[1, 2] and changed[2, 0] and changed.sum() == 2, changed
+    ys = orc.gated_rmsnorm(o2 * 3.5, z, w, eps=0.0)
+    _close(ys, orc.gated_rmsnorm(o2, z, w, eps=0.0), 1e-14, what="scale invariance")
+
+
 CONV_PINS = [pin_conv_numpy, pin_conv_window, pin_conv_f32]
-ALL_PINS = RECURRENCE_PINS + CONV_PINS
+NORM_PINS = [pin_gated_norm_closed_forms, pin_gated_norm_gate, pin_gated_norm_rows_independent]
+ALL_PINS = RECURRENCE_PINS + CONV_PINS + NORM_PINS

@@ -30,6 +30,11 @@ MUTANTS = [
     ("f32 conv taps reversed", "acc = fmaf(w[c * W + j], xv, acc);", "acc = fmaf(w[c * W + (W - 1 - j)], xv, acc);"),
     ("exp coefficient", "p = fmaf(p, r, (float)(1.0 / 6.0));", "p = fmaf(p, r, (float)(1.0 / 7.0));"),
     ("exp reduction", "r = fmaf(-n, c2, r);", "r = r;"),
+    ("norm sum for mean", "sqrt(ss / d + eps)", "sqrt(ss + eps)"),
+    ("norm eps outside", "sqrt(ss / d + eps)", "(sqrt(ss / d) + eps)"),
+    ("norm weight dropped", "y[r * d + j] = w[j] * orow[j]", "y[r * d + j] = orow[j]"),
+    ("norm gate as sigmoid", "inv_rms * silu_f64(zrow[j])", "inv_rms * silu_f64(zrow[j]) / zrow[j]"),
+    ("norm over all rows", "ss += orow[j] * orow[j];", "ss += o[j] * o[j];"),
 ]
 
 
