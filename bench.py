@@ -64,6 +64,11 @@ def decode_alg_bytes(B, hk, hv, dk, dv, esize=2):
     return 2 * B * hv * dk * dv * 4 + B * (2 * hk * dk + 2 * hv * dv) * esize + 2 * B * hv * 4
 
 
+def gated_norm_alg_bytes(T, hv, dv, esize=2):
+    """o and the gate z read, y written, and the fp32 weight."""
+    return 3 * T * hv * dv * esize + dv * 4
+
+
 def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
     """The fused step: state read and written, the raw row and the conv
     window (read and written) in, o out, g and beta, and the conv taps."""
@@ -74,14 +79,16 @@ def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
 
 KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
                   "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip", "conv_math.h"],
-                  "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"]}
+                  "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"],
+                  "gated_norm": ["gated_norm.hip"]}
 # The GPU kernels each library call launches on the 4096-token bf16 layer
 # (conv_prepare: the convolution, then the chunk prepare; the scan call runs
 # the segment-parallel carry: two passes and a combine) and on the
 # 64-sequence decode step (two calls, or the one fused call).
 CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
                 "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
-                "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"]}
+                "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"],
+                "gated_norm": ["k_gated_norm"]}
 
 
 def source_digest(kernel=None):
@@ -176,6 +183,12 @@ def main():
         o = torch.empty((T, sh.num_v_heads, sh.head_dim_v), dtype=torch.bfloat16, device=dev)
         st = torch.empty((1, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v), dtype=torch.float32, device=dev)
         sets.append(dict(x=x, y=y, g=g, beta=beta, o=o, st=st))
+    # the gated norm's gate and weight (the step after the scan, timed on its own)
+    zn, wn = synth.gate_inputs(5, T, sh.num_v_heads, sh.head_dim_v, "bf16")
+    wn = torch.from_numpy(wn).to(dev)
+    for s_ in sets:
+        s_["z"] = torch.from_numpy(zn).to(torch.bfloat16).to(dev)
+        s_["yn"] = torch.empty_like(s_["o"])
     # one bound problem (dims + workspace) serves every buffer set
     cp = gdn.ConvPrefill(sets[0]["x"], w, num_qk_heads=sh.num_qk_heads, num_v_heads=sh.num_v_heads,
                          head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, seqlen=T, chunk_size=64)
@@ -237,6 +250,17 @@ def main():
     nb = max(args.steps, 20)
     k_cp = back_to_back(lambda s: cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"]), nb)
     k_scan = back_to_back(lambda s: cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"]), nb)
+    norm = gdn.GatedNorm(sets[0]["o"], sets[0]["z"], wn, y=sets[0]["yn"])
+    for i in range(nsets):  # its first launches, before the timed run
+        norm(sets[i]["o"], sets[i]["z"], sets[i]["yn"])
+    k_norm = back_to_back(lambda s: norm(s["o"], s["z"], s["yn"]), nb)
+    B_norm = gated_norm_alg_bytes(T, sh.num_v_heads, sh.head_dim_v)
+    gated_norm = {"gated_norm_us": round(k_norm, 2),
+                  "roofline": {"bound": "hbm", "kernel": "gated_norm", "gpu_kernels": CALL_KERNELS["gated_norm"],
+                               "achieved": round(B_norm / (k_norm * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(B_norm / (k_norm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "traffic": read_traffic("gated_norm", inp.name), "alg_bytes_per_launch": int(B_norm),
+                               "avg_launch_us": round(k_norm, 2)}}
 
     # warm figure: one buffer set, back to back (MALL may serve it)
     warm_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
@@ -421,6 +445,7 @@ def main():
                          "mfma_frac_bf16": round(F_pre / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "alg_bytes": int(B_pre), "alg_flops": int(F_pre)},
         "warm_single_set_us": {"conv_prepare": round(warm_cp, 2), "prefill_scan": round(warm_scan, 2)},
+        "gated_norm": gated_norm,
         "decode": decode,
         "source_digest": {k: source_digest(k) for k in KERNEL_SOURCES},
     }

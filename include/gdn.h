@@ -299,6 +299,30 @@ gdn_status gdn_decode_conv_step(const gdn_dims *d, int32_t conv_width,
                                 const int32_t *state_slots, void *o,
                                 void *stream);
 
+/*
+ * The gated RMS norm on the layer's output, the step before the output
+ * projection (oxydllm notes, "Performance": the Gated DeltaNet's gated norm
+ * runs as one fused kernel over the token batch; "New Features", GGUF
+ * qwen35: its weight is used as stored, with no plus-one).  Per token t and
+ * v-head h, over the head_dim values of that row:
+ *     y[t][h][j] = weight[j] * o[t][h][j] / sqrt(mean_i o[t][h][i]^2 + eps)
+ *                  * silu(z[t][h][j]),   silu(a) = a / (1 + e^-a).
+ *
+ * total_tokens: rows of o, z and y (0 queues nothing).  num_heads: H_v in
+ * [1, 4096]; head_dim: d_v, 64 or 128; dtype: of o, z and y.  o, z, y:
+ * [total_tokens][num_heads][head_dim] with token strides stride_o,
+ * stride_z, stride_y (elements, >= num_heads * head_dim, multiples of 16
+ * bytes), 16-byte aligned; the heads of a token are packed.  weight: fp32
+ * [head_dim], shared by all heads.  eps: finite, >= 0.  y may be o itself
+ * (same pointer and stride: the norm in place) but must not otherwise
+ * overlap o or z.  Arithmetic in fp32; a bf16 y is rounded to nearest even.
+ */
+gdn_status gdn_gated_rmsnorm(int32_t total_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t dtype, const void *o,
+                             int64_t stride_o, const void *z, int64_t stride_z,
+                             const float *weight, float eps, void *y,
+                             int64_t stride_y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

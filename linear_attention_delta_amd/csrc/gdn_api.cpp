@@ -599,4 +599,55 @@ gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const voi
   return ok();
 }
 
+gdn_status gdn_gated_rmsnorm(int32_t total_tokens, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                             const void* o, int64_t stride_o, const void* z, int64_t stride_z, const float* weight,
+                             float eps, void* y, int64_t stride_y, void* stream) {
+  if (total_tokens < 0 || total_tokens > kMaxTokens) return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range");
+  if (num_heads < 1 || num_heads > 4096) return fail(GDN_ERR_INVALID_ARG, "num_heads must be in [1, 4096]");
+  if (head_dim != 64 && head_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_INVALID_ARG, "dtype must be GDN_F32 or GDN_BF16");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int vec = dtype == GDN_BF16 ? 8 : 4;
+  const int64_t row = (int64_t)num_heads * head_dim;
+  if (stride_o < row || stride_z < row || stride_y < row || stride_o % vec || stride_z % vec || stride_y % vec)
+    return fail(GDN_ERR_INVALID_ARG, "token strides must be >= %lld and multiples of %d elements", (long long)row, vec);
+  if (!weight || !aligned(weight, 4)) return fail(GDN_ERR_INVALID_ARG, "weight must be non-NULL and 4-byte aligned");
+  if (total_tokens > 0) {
+    if (!o || !z || !y) return fail(GDN_ERR_INVALID_ARG, "o, z and y must be non-NULL");
+    if (!aligned(o, 16) || !aligned(z, 16) || !aligned(y, 16))
+      return fail(GDN_ERR_INVALID_ARG, "o, z and y must be 16-byte aligned");
+    const size_t esz = elem_size(dtype);
+    auto span = [&](int64_t stride) { return ((size_t)(total_tokens - 1) * stride + row) * esz; };
+    auto overlap = [](const void* p, size_t pn, const void* q, size_t qn) {
+      const char* a = reinterpret_cast<const char*>(p);
+      const char* b = reinterpret_cast<const char*>(q);
+      return a < b + qn && b < a + pn;
+    };
+    if (overlap(y, span(stride_y), z, span(stride_z))) return fail(GDN_ERR_INVALID_ARG, "y must not overlap z");
+    if (!(y == o && stride_y == stride_o) && overlap(y, span(stride_y), o, span(stride_o)))
+      return fail(GDN_ERR_INVALID_ARG, "y may be o itself (same stride) but must not partially overlap it");
+  }
+  gdn::NormArgs a;
+  a.rows = (long)total_tokens * num_heads;
+  a.heads = num_heads;
+  a.dv = head_dim;
+  a.dtype = dtype;
+  a.o = o;
+  a.z = z;
+  a.weight = weight;
+  a.y = y;
+  a.stride_o = stride_o;
+  a.stride_z = stride_z;
+  a.stride_y = stride_y;
+  a.eps = eps;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_gated_norm(a, s);
+  if (e != hipSuccess) return hip_fail(e, "gated norm launch");
+  if (debug_enabled() && total_tokens > 0) {
+    gdn_status st = debug_check(s, "gated norm y", y, (long)(total_tokens - 1) * stride_y + row, dtype);
+    if (st != GDN_OK) return st;
+  }
+  return ok();
+}
+
 }  // extern "C"

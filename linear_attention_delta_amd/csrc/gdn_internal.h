@@ -65,7 +65,21 @@ struct ScanArgs {
   int num_slots;
 };
 
+// Gated RMS norm over rows of d_v values (one row per token and v-head;
+// heads packed inside a token row); device pointers.
+struct NormArgs {
+  long rows;       // tokens * heads
+  int heads, dv, dtype;
+  const void* o;
+  const void* z;
+  const float* weight;
+  void* y;
+  long stride_o, stride_z, stride_y;  // elements between tokens
+  float eps;
+};
+
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
+hipError_t launch_gated_norm(const NormArgs& a, hipStream_t s);
 hipError_t launch_chunk_table(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prepare(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);

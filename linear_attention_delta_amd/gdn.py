@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
-            "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step"]
+            "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
+            "gdn_gated_rmsnorm"]
 
 
 class GdnDims(ctypes.Structure):
@@ -68,6 +69,7 @@ def _load():
         "gdn_prefill_conv_chunked": ([D, i32, P, i64, P, P, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
         "gdn_decode_conv_step": ([D, i32, P, i64, P, P, P, P, P, P, i32, P, P, P], i32),
+        "gdn_gated_rmsnorm": ([i32, i32, i32, i32, P, i64, P, i64, P, ctypes.c_float, P, i64, P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -402,4 +404,38 @@ def decode_conv_step(x, weight, g, beta, state, conv_state, *, num_qk_heads, num
     _check(lib.gdn_decode_conv_step(ctypes.byref(d), weight.shape[1], _ptr(x), x.stride(0), _ptr(weight), _ptr(bias),
                                     _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), state.shape[0],
                                     _ptr(state_slots), _ptr(out), _stream(stream)))
+    return out
+
+
+class GatedNorm:
+    """Bound gated-norm call: sizes, strides, weight and stream fixed at
+    construction from example o, z and y views, so that a loop of calls pays
+    only the library call itself."""
+
+    def __init__(self, o, z, weight, *, y=None, eps=1e-6, stream=None):
+        n, h, d = o.shape
+        ys = _row_stride(y) if y is not None else h * d
+        self._fixed = (n, h, d, _dtype_code(o))
+        self._strides = (_row_stride(o), _row_stride(z), ys)
+        self._w = (_ptr(weight), ctypes.c_float(eps))
+        self._keep = weight
+        self._stream = _stream(stream)
+
+    def __call__(self, o, z, y):
+        so, sz, sy = self._strides
+        _check(lib.gdn_gated_rmsnorm(*self._fixed, o.data_ptr(), so, z.data_ptr(), sz, *self._w, y.data_ptr(), sy,
+                                     self._stream))
+        return y
+
+
+def gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None, stream=None):
+    """Gated RMS norm of the layer output: o, z [N_tok, H_v, d_v] (token rows
+    may be strided views), weight fp32 [d_v].  out may be o (in place).
+    Returns y = weight * o / rms(o) * silu(z) per (token, head)."""
+    import torch
+    n, h, d = o.shape
+    if out is None:
+        out = torch.empty((n, h, d), dtype=o.dtype, device=o.device)
+    _check(lib.gdn_gated_rmsnorm(n, h, d, _dtype_code(o), _ptr(o), _row_stride(o), _ptr(z), _row_stride(z),
+                                 _ptr(weight), float(eps), _ptr(out), _row_stride(out), _stream(stream)))
     return out

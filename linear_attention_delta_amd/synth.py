@@ -244,3 +244,12 @@ def split_qkv(y: np.ndarray, shape: LayerShape):
     k = y[:, a:2 * a].reshape(n, shape.num_qk_heads, shape.head_dim_k)
     v = y[:, 2 * a:].reshape(n, shape.num_v_heads, shape.head_dim_v)
     return q, k, v
+
+
+def gate_inputs(seed: int, n_tok: int, hv: int, dv: int, dtype: str):
+    """The gated norm's other inputs: the gate projection z ~ N(0, 1) in the
+    input dtype [n_tok][hv][dv], and an fp32 weight [dv] ~ 1 + N(0, 0.1)."""
+    r = _rng(seed, "gate")
+    z = _quant(r.normal(size=(n_tok, hv, dv)).astype(np.float32), dtype)
+    w = (1.0 + 0.1 * r.normal(size=dv)).astype(np.float32)
+    return z, w

@@ -198,3 +198,24 @@ def test_decode_conv_step_rejects_before_any_gpu_call(g):
     assert L.gdn_decode_conv_step(ctypes.byref(d), 4, X, cc, W, None, CS, 0, B, S, 4, None, O, None) == 1  # no g
     d8 = _dims(g, num_seqs=4, total_tokens=4, seqlen=1, num_qk_heads=4, num_v_heads=32)
     assert step(dd=d8, sx=2 * 4 * 128 + 32 * 128) == 2   # 8 v-heads per q/k head: not supported fused
+
+
+def test_gated_rmsnorm_rejects_before_any_gpu_call(g):
+    L = g.lib
+    row = 32 * 128
+    O, Z, Y, W = 1 << 32, 1 << 36, 1 << 40, 1 << 41   # fake, aligned, disjoint
+
+    def norm(n=16, h=32, d=128, dt=1, o=O, so=row, z=Z, sz=row, w=W, eps=1e-6, y=Y, sy=row):
+        return L.gdn_gated_rmsnorm(n, h, d, dt, o, so, z, sz, w, eps, y, sy, None)
+
+    assert norm(d=96) == 2                          # head dim
+    assert norm(h=0) == 1 and norm(n=-1) == 1
+    assert norm(dt=3) == 1
+    assert norm(eps=-1.0) == 1 and norm(eps=float("nan")) == 1
+    assert norm(so=row - 8) == 1 and norm(sz=row + 4) == 1   # short row; not a multiple of 8 bf16
+    assert norm(w=0) == 1                           # no weight
+    assert norm(o=O + 2) == 1                       # misaligned
+    assert norm(y=Z + 64) == 1                      # y overlaps z
+    assert norm(y=O + 16 * 2) == 1                  # y partially overlaps o
+    assert norm(y=O, sy=row + 8) == 1               # y is o with another stride
+    assert norm(n=0, o=0, z=0, y=0) == 0            # nothing to do: no launch, no pointers needed

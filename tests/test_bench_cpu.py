@@ -43,6 +43,11 @@ def test_conv_prepare_and_decode_bytes():
     assert bench.decode_conv_alg_bytes(64, 16, 32, 128, 128, W=4) == fused == 276_447_232
 
 
+def test_gated_norm_bytes():
+    # o and z read, y written (4096 tokens x 32 heads x 128, bf16), plus the fp32 weight
+    assert bench.gated_norm_alg_bytes(4096, 32, 128) == 3 * 4096 * 32 * 128 * 2 + 128 * 4 == 100_663_808
+
+
 def test_call_kernels_exist_in_their_sources():
     csrc = os.path.join(ROOT, "linear_attention_delta_amd", "csrc")
     for call, kernels in bench.CALL_KERNELS.items():
