@@ -54,6 +54,8 @@ class Oracle:
         lib.gdn_oracle_scan.restype = i32
         lib.gdn_oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i32, P, P, P, ctypes.c_double, P]
         lib.gdn_oracle_gated_rmsnorm.restype = None
+        lib.gdn_oracle_gating.argtypes = [ctypes.c_long, i32, P, P, P, P, P, P]
+        lib.gdn_oracle_gating.restype = None
         lib.gdn_oracle_available_cores.argtypes = []
         lib.gdn_oracle_available_cores.restype = i32
         self.lib = lib
@@ -137,6 +139,17 @@ class Oracle:
         self.lib.gdn_oracle_gated_rmsnorm(o.size // d if d else 0, d, _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y))
         return y
 
+    def gating(self, a, b, A_log, dt_bias):
+        """Gates in fp64 from the raw projections a, b [N][H] and the per-head
+        A_log, dt_bias [H].  Returns (g, beta), each [N][H]."""
+        a, b, A_log, dt_bias = (_f64(x) for x in (a, b, A_log, dt_bias))
+        assert a.ndim == 2 and b.shape == a.shape and A_log.shape == dt_bias.shape == (a.shape[1],)
+        g = np.zeros(a.shape, dtype=np.float64)
+        beta = np.zeros(a.shape, dtype=np.float64)
+        self.lib.gdn_oracle_gating(a.shape[0], a.shape[1], _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                   _ptr(g), _ptr(beta))
+        return g, beta
+
     def decode_step(self, q, k, v, g, beta, state, *, scale=1.0, l2norm=True, heads_tiled=False,
                     n_threads=0):
         """One recurrent step for B sequences (one token each): q, k [B][H_k][d_k],
@@ -200,6 +213,10 @@ def decode_step(*a, **kw):
 
 def gated_rmsnorm(*a, **kw):
     return default().gated_rmsnorm(*a, **kw)
+
+
+def gating(*a, **kw):
+    return default().gating(*a, **kw)
 
 
 def source_text() -> str:

@@ -59,6 +59,14 @@
  *        y_j = w_j * o_j / sqrt(mean_i o_i^2 + eps) * silu(z_j),
  *    silu(a) = a / (1 + e^-a): normalise first, then gate.
  *
+ *  - gdn_oracle_gating: the per-token gates from the layer's small raw
+ *    projections (the oxydllm notes, "Performance": the beta and decay
+ *    projections; "New Features", GGUF qwen35: the per-head decay rate is
+ *    stored as the negated exponential of A_log).  Per token t and v-head h:
+ *        g    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *        beta = 1 / (1 + exp(-b[t][h]))
+ *    softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|).
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread -lm.
  * -ffp-contract=off matters: the fp32 convolution must not gain or lose
  * fused multiply-adds behind the source's back.
@@ -324,4 +332,20 @@ void gdn_oracle_gated_rmsnorm(long rows, int d, const double *o, const double *z
         const double inv_rms = 1.0 / sqrt(ss / d + eps);
         for (int j = 0; j < d; j++) y[r * d + j] = w[j] * orow[j] * inv_rms * silu_f64(zrow[j]);
     }
+}
+
+/* --------------------------------------------------------------- gating */
+
+static double softplus_f64(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+/* a, b, g, beta: [n_tok][H]; A_log, dt_bias: [H]. */
+void gdn_oracle_gating(long n_tok, int H, const double *a, const double *b, const double *A_log,
+                       const double *dt_bias, double *g, double *beta)
+{
+    for (long t = 0; t < n_tok; t++)
+        for (int h = 0; h < H; h++) {
+            const long i = t * H + h;
+            g[i] = -exp(A_log[h]) * softplus_f64(a[i] + dt_bias[h]);
+            beta[i] = 1.0 / (1.0 + exp(-b[i]));
+        }
 }

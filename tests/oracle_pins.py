@@ -491,6 +491,54 @@ def pin_gated_norm_rows_independent(orc):
     _close(ys, orc.gated_rmsnorm(o2, z, w, eps=0.0), 1e-14, what="scale invariance")
 
 
+# ------------------------------------------------------------------ gating
+# g = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b), per (token, v-head).
+
+def pin_gating_closed_forms(orc):
+    """Points where softplus and the sigmoid are known: softplus(0) = ln 2,
+    softplus(ln(e - 1)) = 1, softplus(x) -> x and -> e^x at the ends;
+    sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4, 1/4."""
+    H = 3
+    A_log = np.array([0.0, math.log(2.0), -1.0])
+    dt_bias = np.array([0.0, 0.5, -0.25])
+    pre = np.array([[0.0, math.log(math.e - 1.0), 50.0], [-50.0, 0.0, 0.0]])   # a + dt_bias
+    a = pre - dt_bias
+    b = np.array([[0.0, math.log(3.0), -math.log(3.0)], [0.0, 0.0, 0.0]])
+    g, beta = orc.gating(a, b, A_log, dt_bias)
+    decay = np.exp(A_log)
+    sp = np.array([[math.log(2.0), 1.0, 50.0], [math.exp(-50.0), math.log(2.0), math.log(2.0)]])
+    _close(g, -decay * sp, 1e-12, what="g closed forms")
+    assert abs(g[1, 0] / (-math.exp(-50.0)) - 1.0) < 1e-12, g[1, 0]     # relative, far below 1
+    _close(beta, [[0.5, 0.75, 0.25], [0.5, 0.5, 0.5]], 1e-14, what="beta closed forms")
+    assert H == g.shape[1]
+
+
+def pin_gating_heads_and_ranges(orc):
+    """Each head takes its own A_log and dt_bias (a head's gates move with its
+    own parameters only); g <= 0 and 0 < beta < 1; g is monotone decreasing
+    in a and beta increasing in b."""
+    r = _rng(50)
+    T, H = 7, 5
+    a = r.normal(size=(T, H)) * 3
+    b = r.normal(size=(T, H)) * 3
+    A_log = r.normal(size=H)
+    dt_bias = r.normal(size=H)
+    g0, b0 = orc.gating(a, b, A_log, dt_bias)
+    assert np.all(g0 < 0) and np.all((b0 > 0) & (b0 < 1))
+    A2, d2 = A_log.copy(), dt_bias.copy()
+    A2[3] += 0.7
+    d2[1] -= 1.3
+    g1, b1 = orc.gating(a, b, A2, d2)
+    moved = np.any(g1 != g0, axis=0)
+    assert moved[1] and moved[3] and moved.sum() == 2, moved
+    assert np.array_equal(b1, b0)
+    _close(g1[:, 3], g0[:, 3] * math.exp(0.7), 1e-13, what="A_log scales the decay rate")
+    ga, _ = orc.gating(a + 0.5, b, A_log, dt_bias)
+    _, bb = orc.gating(a, b + 0.5, A_log, dt_bias)
+    assert np.all(ga < g0) and np.all(bb > b0)
+
+
 CONV_PINS = [pin_conv_numpy, pin_conv_window, pin_conv_f32]
 NORM_PINS = [pin_gated_norm_closed_forms, pin_gated_norm_gate, pin_gated_norm_rows_independent]
-ALL_PINS = RECURRENCE_PINS + CONV_PINS + NORM_PINS
+GATING_PINS = [pin_gating_closed_forms, pin_gating_heads_and_ranges]
+ALL_PINS = RECURRENCE_PINS + CONV_PINS + NORM_PINS + GATING_PINS

@@ -35,6 +35,13 @@ MUTANTS = [
     ("norm weight dropped", "y[r * d + j] = w[j] * orow[j]", "y[r * d + j] = orow[j]"),
     ("norm gate as sigmoid", "inv_rms * silu_f64(zrow[j])", "inv_rms * silu_f64(zrow[j]) / zrow[j]"),
     ("norm over all rows", "ss += orow[j] * orow[j];", "ss += o[j] * o[j];"),
+    ("gating softplus as exp", "-exp(A_log[h]) * softplus_f64(a[i] + dt_bias[h])", "-exp(A_log[h]) * exp(a[i] + dt_bias[h])"),
+    ("gating A_log not exponentiated", "-exp(A_log[h]) * softplus_f64", "-A_log[h] * softplus_f64"),
+    ("gating sign", "g[i] = -exp(A_log[h])", "g[i] = exp(A_log[h])"),
+    ("gating bias dropped", "softplus_f64(a[i] + dt_bias[h])", "softplus_f64(a[i])"),
+    ("gating bias of head 0", "softplus_f64(a[i] + dt_bias[h])", "softplus_f64(a[i] + dt_bias[0])"),
+    ("beta sign", "beta[i] = 1.0 / (1.0 + exp(-b[i]));", "beta[i] = 1.0 / (1.0 + exp(b[i]));"),
+    ("softplus large-x branch", "(x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)))", "log1p(exp(-fabs(x)))"),
 ]
 
 
