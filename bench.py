@@ -69,6 +69,11 @@ def gated_norm_alg_bytes(T, hv, dv, esize=2):
     return 3 * T * hv * dv * esize + dv * 4
 
 
+def gating_alg_bytes(T, hv, esize=2):
+    """a and b read, g and beta (fp32) written, and the two fp32 parameters."""
+    return 2 * T * hv * esize + 2 * T * hv * 4 + 2 * hv * 4
+
+
 def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
     """The fused step: state read and written, the raw row and the conv
     window (read and written) in, o out, g and beta, and the conv taps."""
@@ -80,7 +85,7 @@ def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
 KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
                   "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip", "conv_math.h"],
                   "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"],
-                  "gated_norm": ["gated_norm.hip"]}
+                  "gated_norm": ["gated_norm.hip"], "gating": ["gating.hip"]}
 # The GPU kernels each library call launches on the 4096-token bf16 layer
 # (conv_prepare: the convolution, then the chunk prepare; the scan call runs
 # the segment-parallel carry: two passes and a combine) and on the
@@ -88,7 +93,7 @@ KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
 CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
                 "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
                 "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"],
-                "gated_norm": ["k_gated_norm"]}
+                "gated_norm": ["k_gated_norm"], "gating": ["k_gating"]}
 
 
 def source_digest(kernel=None):
@@ -186,9 +191,16 @@ def main():
     # the gated norm's gate and weight (the step after the scan, timed on its own)
     zn, wn = synth.gate_inputs(5, T, sh.num_v_heads, sh.head_dim_v, "bf16")
     wn = torch.from_numpy(wn).to(dev)
+    # and the gates' raw projections (the step before it)
+    abn, A_log, dt_bias = synth.gating_inputs(6, T, sh.num_v_heads, "bf16")
+    A_log, dt_bias = torch.from_numpy(A_log).to(dev), torch.from_numpy(dt_bias).to(dev)
     for s_ in sets:
         s_["z"] = torch.from_numpy(zn).to(torch.bfloat16).to(dev)
         s_["yn"] = torch.empty_like(s_["o"])
+        s_["ab"] = torch.from_numpy(abn).to(torch.bfloat16).to(dev)
+        s_["a_"], s_["b_"] = s_["ab"][:, :sh.num_v_heads], s_["ab"][:, sh.num_v_heads:]
+        s_["gg"] = torch.empty_like(s_["g"])
+        s_["bg"] = torch.empty_like(s_["beta"])
     # one bound problem (dims + workspace) serves every buffer set
     cp = gdn.ConvPrefill(sets[0]["x"], w, num_qk_heads=sh.num_qk_heads, num_v_heads=sh.num_v_heads,
                          head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, seqlen=T, chunk_size=64)
@@ -255,6 +267,25 @@ def main():
         norm(sets[i]["o"], sets[i]["z"], sets[i]["yn"])
     k_norm = back_to_back(lambda s: norm(s["o"], s["z"], s["yn"]), nb)
     B_norm = gated_norm_alg_bytes(T, sh.num_v_heads, sh.head_dim_v)
+    hv_ = sh.num_v_heads
+    gate = gdn.Gating(sets[0]["a_"], sets[0]["b_"], A_log, dt_bias)
+    for i in range(nsets):
+        gate(sets[i]["a_"], sets[i]["b_"], sets[i]["gg"], sets[i]["bg"])
+    k_gate = back_to_back(lambda s: gate(s["a_"], s["b_"], s["gg"], s["bg"]), nb)
+    B_gate = gating_alg_bytes(T, hv_)
+    # the whole prefill from the raw projections in one call, the gates
+    # computed in the prepare (against gating + conv_prepare + scan)
+    for s_ in sets:
+        s_["gates"] = gdn.gate_inputs(s_["a_"], s_["b_"], A_log, dt_bias)
+    k_gated = back_to_back(lambda s: gdn.conv_prefill_gated(cp, s["x"], s["y"], s["gates"], s["o"],
+                                                            state_out=s["st"]), nb)
+    gating = {"gating_us": round(k_gate, 2), "prefill_conv_gated_us": round(k_gated, 2),
+              "prefill_gating_then_calls_us": round(k_gate + k_cp + k_scan, 2),
+              "roofline": {"bound": "hbm", "kernel": "gating", "gpu_kernels": CALL_KERNELS["gating"],
+                           "achieved": round(B_gate / (k_gate * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(B_gate / (k_gate * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": read_traffic("gating", inp.name), "alg_bytes_per_launch": int(B_gate),
+                           "avg_launch_us": round(k_gate, 2)}}
     gated_norm = {"gated_norm_us": round(k_norm, 2),
                   "roofline": {"bound": "hbm", "kernel": "gated_norm", "gpu_kernels": CALL_KERNELS["gated_norm"],
                                "achieved": round(B_norm / (k_norm * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
@@ -446,6 +477,7 @@ def main():
                          "alg_bytes": int(B_pre), "alg_flops": int(F_pre)},
         "warm_single_set_us": {"conv_prepare": round(warm_cp, 2), "prefill_scan": round(warm_scan, 2)},
         "gated_norm": gated_norm,
+        "gating": gating,
         "decode": decode,
         "source_digest": {k: source_digest(k) for k in KERNEL_SOURCES},
     }

@@ -90,6 +90,22 @@ typedef struct gdn_dims {
     int64_t stride_v;     /* same for v; 0 = H_v*d_v */
 } gdn_dims;
 
+/*
+ * The gates' raw inputs, for the calls that compute g and beta themselves
+ * (see gdn_gating for the map): the decay and beta projections a, b
+ * [N_tok][H_v] in the problem's dtype with token strides stride_a, stride_b
+ * (elements, >= H_v; they may be column blocks of one projection output),
+ * aligned to their element size, and the fp32 per-head A_log, dt_bias [H_v].
+ */
+typedef struct gdn_gate_inputs {
+    const void *a;
+    int64_t stride_a;
+    const void *b;
+    int64_t stride_b;
+    const float *A_log;
+    const float *dt_bias;
+} gdn_gate_inputs;
+
 /* Human-readable name of a status code (static storage). */
 const char *gdn_status_string(gdn_status s);
 
@@ -322,6 +338,67 @@ gdn_status gdn_gated_rmsnorm(int32_t total_tokens, int32_t num_heads,
                              int64_t stride_o, const void *z, int64_t stride_z,
                              const float *weight, float eps, void *y,
                              int64_t stride_y, void *stream);
+
+/*
+ * The per-token gates from the layer's small raw projections (oxydllm
+ * notes, "Performance": the beta and decay projections; "New Features",
+ * GGUF qwen35: the per-head decay rate is the negated exponential of A_log,
+ * and the scalar parameters stay fp32).  Per token t and v-head h:
+ *     g[t][h]    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *     beta[t][h] = 1 / (1 + exp(-b[t][h]))
+ * softplus(x) = log(1 + e^x).  g (a log-decay, <= 0) and beta are what the
+ * prefill and decode calls take.
+ *
+ * total_tokens: rows (0 queues nothing).  num_heads: H_v in [1, 4096].
+ * dtype: of a and b.  a, b: [total_tokens][num_heads] with token strides
+ * stride_a, stride_b (elements, >= num_heads; they may be column blocks of
+ * one projection output), aligned to their element size.  A_log, dt_bias:
+ * fp32 [num_heads].  g, beta: fp32 [total_tokens][num_heads], packed,
+ * 4-byte aligned, overlapping neither each other nor a or b.  Arithmetic in
+ * fp32 with the accurate exponential and log1p.
+ */
+gdn_status gdn_gating(int32_t total_tokens, int32_t num_heads, int32_t dtype,
+                      const void *a, int64_t stride_a, const void *b,
+                      int64_t stride_b, const float *A_log,
+                      const float *dt_bias, float *g, float *beta,
+                      void *stream);
+
+/*
+ * The whole prefill from the layer's raw projections: gdn_prefill_conv_chunked
+ * with g and beta computed inside the prepare from gates (the gdn_gating map,
+ * the same fp32 arithmetic), so they never go through memory.  The result
+ * equals gdn_gating into g, beta followed by gdn_prefill_conv_chunked with
+ * them, bit for bit.  gates: see gdn_gate_inputs, required.  Every other
+ * argument as gdn_prefill_conv_chunked.
+ */
+gdn_status gdn_prefill_conv_gated(const gdn_dims *d,
+                                  const gdn_gate_inputs *gates,
+                                  int32_t conv_width, const void *x,
+                                  int64_t stride_x, const float *conv_weight,
+                                  const float *conv_bias, void *conv_state,
+                                  const float *state_in,
+                                  const int32_t *cu_seqlens, void *y,
+                                  int64_t stride_y, void *o, float *state_out,
+                                  void *workspace, size_t ws_bytes,
+                                  void *stream);
+
+/*
+ * One decode step from the layer's raw projections: gdn_decode_conv_step
+ * with g and beta computed in the step's kernel from gates (one token per
+ * sequence: a and b are [B][H_v] rows).  Equals gdn_gating followed by
+ * gdn_decode_conv_step, bit for bit.  gates: required; every other argument
+ * as gdn_decode_conv_step.
+ */
+gdn_status gdn_decode_conv_gated_step(const gdn_dims *d,
+                                      const gdn_gate_inputs *gates,
+                                      int32_t conv_width, const void *x,
+                                      int64_t stride_x,
+                                      const float *conv_weight,
+                                      const float *conv_bias,
+                                      void *conv_state, float *state,
+                                      int32_t num_slots,
+                                      const int32_t *state_slots, void *o,
+                                      void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "conv_math.h"
+#include "gate_math.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -277,8 +278,13 @@ __global__ void __launch_bounds__(1024) k_decode_conv(ScanArgs a, ConvArgs c) {
     }
     if (tid < DV) cv.load(xr, win, cc, c.weight, c.bias, chv);
   }
-  const float g = a.g[(long)b * a.hv + h];
-  const float beta = a.beta[(long)b * a.hv + h];
+  float g, beta;
+  if (a.gate_a) {
+    gates_from_raw<E>(a, b, h, g, beta);
+  } else {
+    g = a.g[(long)b * a.hv + h];
+    beta = a.beta[(long)b * a.hv + h];
+  }
   if constexpr (kEarly) load_state<DK, DV>(S, rg, cg, s);
 
   // late loads go one channel at a time, to keep fewer values live

@@ -202,18 +202,45 @@ gdn_status debug_check(hipStream_t s, const char* what, const void* p, long n, i
   return GDN_OK;
 }
 
+// need_gb: g and beta are arrays (false where the gates come from the raw
+// projections, checked by check_gates)
 gdn_status check_scan_ptrs(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, const int32_t* cu, bool need_qv) {
+                           const float* beta, const int32_t* cu, bool need_qv, bool need_gb = true) {
   if (d->total_tokens > 0) {
-    if (!k || !g || !beta || (need_qv && (!q || !v)))
+    if (!k || (need_gb && (!g || !beta)) || (need_qv && (!q || !v)))
       return fail(GDN_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
     if (!aligned(k, 16) || (need_qv && (!aligned(q, 16) || !aligned(v, 16))))
       return fail(GDN_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
-    if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_INVALID_ARG, "g and beta must be 4-byte aligned");
+    if (need_gb && (!aligned(g, 4) || !aligned(beta, 4)))
+      return fail(GDN_ERR_INVALID_ARG, "g and beta must be 4-byte aligned");
   }
   if (d->seqlen == 0 && (!cu || !aligned(cu, 4)))
     return fail(GDN_ERR_INVALID_ARG, "varlen (seqlen == 0) needs a 4-byte aligned cu_seqlens");
   return GDN_OK;
+}
+
+gdn_status check_gates(const gdn_dims* d, const gdn_gate_inputs* G) {
+  if (!G) return fail(GDN_ERR_INVALID_ARG, "gates is NULL");
+  if (G->stride_a < d->num_v_heads || G->stride_b < d->num_v_heads)
+    return fail(GDN_ERR_INVALID_ARG, "gate strides must be >= num_v_heads (%d)", d->num_v_heads);
+  if (!G->A_log || !G->dt_bias || !aligned(G->A_log, 4) || !aligned(G->dt_bias, 4))
+    return fail(GDN_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL and 4-byte aligned");
+  if (d->total_tokens > 0) {
+    if (!G->a || !G->b) return fail(GDN_ERR_INVALID_ARG, "gate projections a and b must be non-NULL");
+    if (!aligned(G->a, elem_size(d->dtype)) || !aligned(G->b, elem_size(d->dtype)))
+      return fail(GDN_ERR_INVALID_ARG, "gate projections must be aligned to their element size");
+  }
+  return GDN_OK;
+}
+
+void set_gates(gdn::ScanArgs& a, const gdn_gate_inputs* G) {
+  if (!G) return;
+  a.gate_a = G->a;
+  a.gate_b = G->b;
+  a.stride_ga = G->stride_a;
+  a.stride_gb = G->stride_b;
+  a.A_log = G->A_log;
+  a.dt_bias = G->dt_bias;
 }
 
 gdn_status check_workspace(const gdn_dims* d, const void* ws, size_t ws_bytes) {
@@ -354,12 +381,14 @@ gdn_status gdn_prefill_prepare(const gdn_dims* d, const void* q, const void* k, 
   return ok();
 }
 
-gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+// need_gb false: the carry after a prepare that computed the gates itself
+// (the carry kernels read neither g nor beta)
+static gdn_status scan_impl(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
-                            float* state_out, const void* workspace, size_t ws_bytes, void* stream) {
+                            float* state_out, const void* workspace, size_t ws_bytes, void* stream, bool need_gb) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
-  if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true)) != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true, need_gb)) != GDN_OK) return st;
   if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
@@ -387,6 +416,12 @@ gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, con
   return ok();
 }
 
+gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
+                            float* state_out, const void* workspace, size_t ws_bytes, void* stream) {
+  return scan_impl(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream, true);
+}
+
 gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
                                const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
                                float* state_out, void* workspace, size_t ws_bytes, void* stream) {
@@ -402,10 +437,11 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, 
   return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
 }
 
-gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
-                                    const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
-                                    const float* beta, const int32_t* cu_seqlens, void* y, int64_t stride_y,
-                                    void* workspace, size_t ws_bytes, void* stream) {
+static gdn_status conv_prepare_impl(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,
+                                    const void* x, int64_t stride_x, const float* conv_weight,
+                                    const float* conv_bias, void* conv_state, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, void* y, int64_t stride_y, void* workspace,
+                                    size_t ws_bytes, void* stream) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
   const int64_t cc = 2LL * d->num_qk_heads * d->head_dim_k + (int64_t)d->num_v_heads * d->head_dim_v;
@@ -431,7 +467,8 @@ gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const
   if (conv_state && !aligned(conv_state, 16)) return fail(GDN_ERR_INVALID_ARG, "conv_state must be 16-byte aligned");
   const void* q = y;
   const void* k = reinterpret_cast<const char*>(y) + (size_t)d->num_qk_heads * d->head_dim_k * (d->dtype == GDN_BF16 ? 2 : 4);
-  if ((st = check_scan_ptrs(d, q, k, nullptr, g, beta, cu_seqlens, false)) != GDN_OK) return st;
+  if ((st = check_scan_ptrs(d, q, k, nullptr, g, beta, cu_seqlens, false, !gates)) != GDN_OK) return st;
+  if (gates && (st = check_gates(d, gates)) != GDN_OK) return st;
   if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
 
   gdn::ConvArgs ca;
@@ -457,6 +494,7 @@ gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const
   a.g = g;
   a.beta = beta;
   a.cu_seqlens = cu_seqlens;
+  set_gates(a, gates);
   carve(a, d, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -473,11 +511,19 @@ gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const
   return ok();
 }
 
-gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+gdn_status gdn_prefill_conv_prepare(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
                                     const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
-                                    const float* beta, const float* state_in, const int32_t* cu_seqlens, void* y,
-                                    int64_t stride_y, void* o, float* state_out, void* workspace, size_t ws_bytes,
-                                    void* stream) {
+                                    const float* beta, const int32_t* cu_seqlens, void* y, int64_t stride_y,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return conv_prepare_impl(d, nullptr, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta,
+                           cu_seqlens, y, stride_y, workspace, ws_bytes, stream);
+}
+
+static gdn_status conv_chunked_impl(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,
+                                    const void* x, int64_t stride_x, const float* conv_weight,
+                                    const float* conv_bias, void* conv_state, const float* g, const float* beta,
+                                    const float* state_in, const int32_t* cu_seqlens, void* y, int64_t stride_y,
+                                    void* o, float* state_out, void* workspace, size_t ws_bytes, void* stream) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
   // validate the scan half before queuing anything
@@ -491,15 +537,35 @@ gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, int32_t conv_width, const
     if (a0 < b0 + sbytes && b0 < a0 + sbytes)
       return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
   }
-  if ((st = gdn_prefill_conv_prepare(d, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta,
-                                     cu_seqlens, y, stride_y, workspace, ws_bytes, stream)) != GDN_OK)
+  if ((st = conv_prepare_impl(d, gates, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta,
+                              cu_seqlens, y, stride_y, workspace, ws_bytes, stream)) != GDN_OK)
     return st;
   const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
   const char* y0 = reinterpret_cast<const char*>(y);
   const void* q = y0;
   const void* k = y0 + (size_t)d->num_qk_heads * d->head_dim_k * esz;
   const void* v = y0 + (size_t)2 * d->num_qk_heads * d->head_dim_k * esz;
-  return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
+  return scan_impl(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream, !gates);
+}
+
+gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+                                    const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
+                                    const float* beta, const float* state_in, const int32_t* cu_seqlens, void* y,
+                                    int64_t stride_y, void* o, float* state_out, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  return conv_chunked_impl(d, nullptr, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta, state_in,
+                           cu_seqlens, y, stride_y, o, state_out, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_prefill_conv_gated(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width, const void* x,
+                                  int64_t stride_x, const float* conv_weight, const float* conv_bias, void* conv_state,
+                                  const float* state_in, const int32_t* cu_seqlens, void* y, int64_t stride_y, void* o,
+                                  float* state_out, void* workspace, size_t ws_bytes, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  if ((st = check_gates(d, gates)) != GDN_OK) return st;
+  return conv_chunked_impl(d, gates, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, nullptr, nullptr,
+                           state_in, cu_seqlens, y, stride_y, o, state_out, workspace, ws_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
@@ -532,10 +598,10 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
   return ok();
 }
 
-gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
-                                const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
-                                const float* beta, float* state, int32_t num_slots, const int32_t* state_slots,
-                                void* o, void* stream) {
+static gdn_status decode_conv_impl(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,
+                                   const void* x, int64_t stride_x, const float* conv_weight, const float* conv_bias,
+                                   void* conv_state, const float* g, const float* beta, float* state,
+                                   int32_t num_slots, const int32_t* state_slots, void* o, void* stream) {
   gdn_status st = check_dims(d, 1);
   if (st != GDN_OK) return st;
   const int64_t cc = 2LL * d->num_qk_heads * d->head_dim_k + (int64_t)d->num_v_heads * d->head_dim_v;
@@ -553,8 +619,11 @@ gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const voi
   if (conv_bias && !aligned(conv_bias, 4)) return fail(GDN_ERR_INVALID_ARG, "conv_bias must be 4-byte aligned");
   if (!conv_state || !aligned(conv_state, 16))
     return fail(GDN_ERR_INVALID_ARG, "conv_state must be non-NULL and 16-byte aligned");
-  if (!g || !beta || !aligned(g, 4) || !aligned(beta, 4))
+  if (gates) {
+    if ((st = check_gates(d, gates)) != GDN_OK) return st;
+  } else if (!g || !beta || !aligned(g, 4) || !aligned(beta, 4)) {
     return fail(GDN_ERR_INVALID_ARG, "g and beta must be non-NULL and 4-byte aligned");
+  }
   if (!o || !aligned(o, 16)) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if (!state || !aligned(state, 16)) return fail(GDN_ERR_INVALID_ARG, "state must be non-NULL and 16-byte aligned");
   if (num_slots < 1) return fail(GDN_ERR_INVALID_ARG, "num_slots must be >= 1");
@@ -592,11 +661,31 @@ gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const voi
   a.state = state;
   a.state_slots = state_slots;
   a.num_slots = num_slots;
+  set_gates(a, gates);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gdn::launch_decode_conv(a, c, s);
   if (e != hipSuccess) return hip_fail(e, "decode conv launch");
   if ((st = debug_check(s, "o", o, (long)d->num_seqs * d->num_v_heads * d->head_dim_v, d->dtype)) != GDN_OK) return st;
   return ok();
+}
+
+gdn_status gdn_decode_conv_step(const gdn_dims* d, int32_t conv_width, const void* x, int64_t stride_x,
+                                const float* conv_weight, const float* conv_bias, void* conv_state, const float* g,
+                                const float* beta, float* state, int32_t num_slots, const int32_t* state_slots,
+                                void* o, void* stream) {
+  return decode_conv_impl(d, nullptr, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta, state,
+                          num_slots, state_slots, o, stream);
+}
+
+gdn_status gdn_decode_conv_gated_step(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,
+                                      const void* x, int64_t stride_x, const float* conv_weight,
+                                      const float* conv_bias, void* conv_state, float* state, int32_t num_slots,
+                                      const int32_t* state_slots, void* o, void* stream) {
+  gdn_status st = check_dims(d, 1);
+  if (st != GDN_OK) return st;
+  if ((st = check_gates(d, gates)) != GDN_OK) return st;
+  return decode_conv_impl(d, gates, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, nullptr, nullptr,
+                          state, num_slots, state_slots, o, stream);
 }
 
 gdn_status gdn_gated_rmsnorm(int32_t total_tokens, int32_t num_heads, int32_t head_dim, int32_t dtype,
@@ -646,6 +735,56 @@ gdn_status gdn_gated_rmsnorm(int32_t total_tokens, int32_t num_heads, int32_t he
   if (debug_enabled() && total_tokens > 0) {
     gdn_status st = debug_check(s, "gated norm y", y, (long)(total_tokens - 1) * stride_y + row, dtype);
     if (st != GDN_OK) return st;
+  }
+  return ok();
+}
+
+gdn_status gdn_gating(int32_t total_tokens, int32_t num_heads, int32_t dtype, const void* a, int64_t stride_a,
+                      const void* b, int64_t stride_b, const float* A_log, const float* dt_bias, float* g, float* beta,
+                      void* stream) {
+  if (total_tokens < 0 || total_tokens > kMaxTokens) return fail(GDN_ERR_INVALID_ARG, "total_tokens out of range");
+  if (num_heads < 1 || num_heads > 4096) return fail(GDN_ERR_INVALID_ARG, "num_heads must be in [1, 4096]");
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_INVALID_ARG, "dtype must be GDN_F32 or GDN_BF16");
+  if (stride_a < num_heads || stride_b < num_heads)
+    return fail(GDN_ERR_INVALID_ARG, "token strides must be >= num_heads (%d)", num_heads);
+  if (!A_log || !dt_bias || !aligned(A_log, 4) || !aligned(dt_bias, 4))
+    return fail(GDN_ERR_INVALID_ARG, "A_log and dt_bias must be non-NULL and 4-byte aligned");
+  if (total_tokens > 0) {
+    const size_t esz = elem_size(dtype);
+    if (!a || !b || !g || !beta) return fail(GDN_ERR_INVALID_ARG, "a, b, g and beta must be non-NULL");
+    if (!aligned(a, esz) || !aligned(b, esz) || !aligned(g, 4) || !aligned(beta, 4))
+      return fail(GDN_ERR_INVALID_ARG, "a, b, g and beta must be aligned to their element size");
+    const size_t out = (size_t)total_tokens * num_heads * 4;
+    const size_t ab = ((size_t)(total_tokens - 1) * stride_a + num_heads) * esz;
+    const size_t bb = ((size_t)(total_tokens - 1) * stride_b + num_heads) * esz;
+    auto overlap = [](const void* p, size_t pn, const void* q, size_t qn) {
+      const char* x = reinterpret_cast<const char*>(p);
+      const char* y = reinterpret_cast<const char*>(q);
+      return x < y + qn && y < x + pn;
+    };
+    if (overlap(g, out, beta, out) || overlap(g, out, a, ab) || overlap(g, out, b, bb) || overlap(beta, out, a, ab) ||
+        overlap(beta, out, b, bb))
+      return fail(GDN_ERR_INVALID_ARG, "g and beta must not overlap each other, a or b");
+  }
+  gdn::GatingArgs ga;
+  ga.rows = total_tokens;
+  ga.heads = num_heads;
+  ga.dtype = dtype;
+  ga.gate_a = a;
+  ga.gate_b = b;
+  ga.stride_ga = stride_a;
+  ga.stride_gb = stride_b;
+  ga.A_log = A_log;
+  ga.dt_bias = dt_bias;
+  ga.g = g;
+  ga.beta = beta;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_gating(ga, s);
+  if (e != hipSuccess) return hip_fail(e, "gating launch");
+  if (debug_enabled() && total_tokens > 0) {
+    gdn_status st = debug_check(s, "g", g, (long)total_tokens * num_heads, GDN_F32);
+    if (st != GDN_OK) return st;
+    if ((st = debug_check(s, "beta", beta, (long)total_tokens * num_heads, GDN_F32)) != GDN_OK) return st;
   }
   return ok();
 }

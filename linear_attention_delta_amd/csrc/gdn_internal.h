@@ -63,6 +63,13 @@ struct ScanArgs {
   float* state;
   const int32_t* state_slots;
   int num_slots;
+  // gates from the raw projections (gate_math.h) instead of g and beta,
+  // where gate_a is set: the prepare and the fused decode step compute them
+  const void* gate_a;
+  const void* gate_b;
+  long stride_ga, stride_gb;
+  const float* A_log;
+  const float* dt_bias;
 };
 
 // Gated RMS norm over rows of d_v values (one row per token and v-head;
@@ -78,8 +85,22 @@ struct NormArgs {
   float eps;
 };
 
+// The gates from the raw projections: g, beta fp32 [rows][heads] (packed).
+struct GatingArgs {
+  long rows;  // tokens
+  int heads, dtype;
+  const void* gate_a;
+  const void* gate_b;
+  long stride_ga, stride_gb;  // elements between tokens
+  const float* A_log;
+  const float* dt_bias;
+  float* g;
+  float* beta;
+};
+
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_gated_norm(const NormArgs& a, hipStream_t s);
+hipError_t launch_gating(const GatingArgs& a, hipStream_t s);
 hipError_t launch_chunk_table(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prepare(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);

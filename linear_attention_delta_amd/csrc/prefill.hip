@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "gate_math.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -287,8 +288,12 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
   }
   float gv = 0.f, bv = 0.f;
   if (wave < HPW && lane < len) {
-    gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
-    bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
+    if (a.gate_a) {
+      gates_from_raw<E>(a, start + lane, hs[wave], gv, bv);
+    } else {
+      gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
+      bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
+    }
   }
 
   // ---- stage K and Q into LDS with the per-row inverse norms

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
             "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
-            "gdn_gated_rmsnorm"]
+            "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step"]
 
 
 class GdnDims(ctypes.Structure):
@@ -40,6 +40,11 @@ class GdnDims(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64), ("stride_v", ctypes.c_int64),
     ]
+
+
+class GdnGateInputs(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("stride_a", ctypes.c_int64), ("b", ctypes.c_void_p),
+                ("stride_b", ctypes.c_int64), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
 
 
 class GdnError(RuntimeError):
@@ -55,6 +60,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(GdnDims)
+    GI = ctypes.POINTER(GdnGateInputs)
     sig = {
         "gdn_status_string": ([i32], ctypes.c_char_p),
         "gdn_last_error": ([], ctypes.c_char_p),
@@ -70,6 +76,9 @@ def _load():
         "gdn_decode_step": ([D, P, P, P, P, P, P, i32, P, P, P], i32),
         "gdn_decode_conv_step": ([D, i32, P, i64, P, P, P, P, P, P, i32, P, P, P], i32),
         "gdn_gated_rmsnorm": ([i32, i32, i32, i32, P, i64, P, i64, P, ctypes.c_float, P, i64, P], i32),
+        "gdn_gating": ([i32, i32, i32, P, i64, P, i64, P, P, P, P, P], i32),
+        "gdn_prefill_conv_gated": ([D, GI, i32, P, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
+        "gdn_decode_conv_gated_step": ([D, GI, i32, P, i64, P, P, P, P, i32, P, P, P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -438,4 +447,61 @@ def gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None, stream=None):
         out = torch.empty((n, h, d), dtype=o.dtype, device=o.device)
     _check(lib.gdn_gated_rmsnorm(n, h, d, _dtype_code(o), _ptr(o), _row_stride(o), _ptr(z), _row_stride(z),
                                  _ptr(weight), float(eps), _ptr(out), _row_stride(out), _stream(stream)))
+    return out
+
+
+class Gating:
+    """Bound gating call: sizes, strides, parameters and stream fixed at
+    construction from example a, b views [N_tok, H_v]."""
+
+    def __init__(self, a, b, A_log, dt_bias, *, stream=None):
+        n, h = a.shape
+        self._fixed = (n, h, _dtype_code(a))
+        self._strides = (a.stride(0), b.stride(0))
+        self._p = (_ptr(A_log), _ptr(dt_bias))
+        self._keep = (A_log, dt_bias)
+        self._stream = _stream(stream)
+
+    def __call__(self, a, b, g, beta):
+        sa, sb = self._strides
+        _check(lib.gdn_gating(*self._fixed, a.data_ptr(), sa, b.data_ptr(), sb, *self._p, g.data_ptr(),
+                              beta.data_ptr(), self._stream))
+        return g, beta
+
+
+def gating(a, b, A_log, dt_bias, *, g=None, beta=None, stream=None):
+    """g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b) from the raw
+    projections a, b [N_tok, H_v] (rows may be strided); A_log, dt_bias fp32
+    [H_v].  Returns (g, beta), fp32 [N_tok, H_v]."""
+    import torch
+    n, h = a.shape
+    if g is None:
+        g = torch.empty((n, h), dtype=torch.float32, device=a.device)
+    if beta is None:
+        beta = torch.empty((n, h), dtype=torch.float32, device=a.device)
+    return Gating(a, b, A_log, dt_bias, stream=stream)(a, b, g, beta)
+
+
+def gate_inputs(a, b, A_log, dt_bias) -> GdnGateInputs:
+    """The gates' raw inputs for the gated calls: a, b [N_tok, H_v] views in
+    the problem's dtype (rows may be strided), A_log, dt_bias fp32 [H_v]."""
+    return GdnGateInputs(_ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(A_log), _ptr(dt_bias))
+
+
+def conv_prefill_gated(p: "ConvPrefill", x, y, gates: GdnGateInputs, o, *, state_in=None, state_out=None,
+                       conv_state=None, stream=None):
+    """The whole prefill of a bound ConvPrefill problem with the gates computed
+    in the prepare from their raw projections (gdn_prefill_conv_gated)."""
+    _check(lib.gdn_prefill_conv_gated(ctypes.byref(p.dims), ctypes.byref(gates), p.width, _ptr(x), _row_stride(x),
+                                      _ptr(p.weight), _ptr(p.bias), _ptr(conv_state), _ptr(state_in),
+                                      _ptr(p.cu_seqlens), _ptr(y), p.y_stride, _ptr(o), _ptr(state_out), _ptr(p.ws),
+                                      p.ws_bytes, _stream(stream)))
+
+
+def decode_conv_gated_step(step: "DecodeConv", x, gates: GdnGateInputs, state, conv_state, out, state_slots=None):
+    """One decode step of a bound DecodeConv problem with the gates computed
+    in the step's kernel from their raw projections."""
+    _check(lib.gdn_decode_conv_gated_step(step._d, ctypes.byref(gates), step.width, x.data_ptr(), x.stride(0),
+                                          *step._w, conv_state.data_ptr(), state.data_ptr(), step.num_slots,
+                                          _ptr(state_slots), out.data_ptr(), step._stream))
     return out

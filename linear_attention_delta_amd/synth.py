@@ -253,3 +253,14 @@ def gate_inputs(seed: int, n_tok: int, hv: int, dv: int, dtype: str):
     z = _quant(r.normal(size=(n_tok, hv, dv)).astype(np.float32), dtype)
     w = (1.0 + 0.1 * r.normal(size=dv)).astype(np.float32)
     return z, w
+
+
+def gating_inputs(seed: int, n_tok: int, hv: int, dtype: str):
+    """The gates' raw inputs: the decay and beta projections a, b ~ N(0, 1)
+    as the two column blocks of one [n_tok][2 hv] projection output in the
+    input dtype, and fp32 per-head A_log ~ U(-1, 1.5) and dt_bias ~ N(0, 0.5)."""
+    r = _rng(seed, "gating")
+    ab = _quant(r.normal(size=(n_tok, 2 * hv)).astype(np.float32), dtype)
+    A_log = r.uniform(-1.0, 1.5, size=hv).astype(np.float32)
+    dt_bias = (0.5 * r.normal(size=hv)).astype(np.float32)
+    return ab, A_log, dt_bias

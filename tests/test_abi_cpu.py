@@ -219,3 +219,48 @@ def test_gated_rmsnorm_rejects_before_any_gpu_call(g):
     assert norm(y=O + 16 * 2) == 1                  # y partially overlaps o
     assert norm(y=O, sy=row + 8) == 1               # y is o with another stride
     assert norm(n=0, o=0, z=0, y=0) == 0            # nothing to do: no launch, no pointers needed
+
+
+def test_gating_rejects_before_any_gpu_call(g):
+    L = g.lib
+    A, B, AL, DB, G_, BE = 1 << 32, (1 << 32) + 32, 1 << 36, 1 << 37, 1 << 40, 1 << 41   # fake addresses
+
+    def gate(n=16, h=32, dt=1, a=A, sa=64, b=B, sb=64, al=AL, db=DB, g_=G_, be=BE):
+        return L.gdn_gating(n, h, dt, a, sa, b, sb, al, db, g_, be, None)
+
+    assert gate(h=0) == 1 and gate(n=-1) == 1 and gate(dt=2) == 1
+    assert gate(sa=31) == 1                     # stride below the head count
+    assert gate(al=0) == 1 and gate(db=0) == 1  # parameters required
+    assert gate(a=A + 1) == 1                   # misaligned bf16
+    assert gate(g_=0) == 1
+    assert gate(be=G_ + 64) == 1                # beta overlaps g
+    assert gate(g_=A) == 1                      # g overlaps a
+    assert gate(n=0, a=0, b=0, g_=0, be=0) == 0 # nothing to do
+
+
+def test_gated_calls_reject_before_any_gpu_call(g):
+    L = g.lib
+    cc = 8192
+    d = _dims(g, stride_q=cc, stride_k=cc, stride_v=cc)
+    ws = g.workspace_size(d)
+    X, Y, W, O, AB, AL, DB = 1 << 32, 1 << 36, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44
+
+    def gates(a=AB, sa=64, b=AB + 64, sb=64, al=AL, db=DB):
+        return ctypes.byref(g.GdnGateInputs(a, sa, b, sb, al, db))
+
+    def pre(gt):
+        return L.gdn_prefill_conv_gated(ctypes.byref(d), gt, 4, X, cc, W, None, None, None, None, Y, cc, O, None, 256,
+                                        ws, None)
+
+    assert pre(None) == 1                     # gates required
+    assert pre(gates(sa=31)) == 1             # stride below H_v
+    assert pre(gates(al=0)) == 1 and pre(gates(db=0)) == 1
+    assert pre(gates(a=0)) == 1               # no decay projection
+    assert pre(gates(b=AB + 1)) == 1          # misaligned bf16
+    dd = _dims(g, num_seqs=4, total_tokens=4, seqlen=1)
+
+    def dec(gt, slots=4):
+        return L.gdn_decode_conv_gated_step(ctypes.byref(dd), gt, 4, X, cc, W, None, Y, O, slots, None, 1 << 45, None)
+
+    assert dec(None) == 1 and dec(gates(b=0)) == 1
+    assert dec(gates(), slots=2) == 1         # fewer slots than sequences

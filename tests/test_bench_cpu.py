@@ -48,6 +48,11 @@ def test_gated_norm_bytes():
     assert bench.gated_norm_alg_bytes(4096, 32, 128) == 3 * 4096 * 32 * 128 * 2 + 128 * 4 == 100_663_808
 
 
+def test_gating_bytes():
+    # a, b bf16 in, g, beta fp32 out over 4096 tokens x 32 v-heads, plus A_log and dt_bias
+    assert bench.gating_alg_bytes(4096, 32) == 2 * 4096 * 32 * 2 + 2 * 4096 * 32 * 4 + 2 * 32 * 4 == 1_573_120
+
+
 def test_call_kernels_exist_in_their_sources():
     csrc = os.path.join(ROOT, "linear_attention_delta_amd", "csrc")
     for call, kernels in bench.CALL_KERNELS.items():
