@@ -431,6 +431,70 @@ def main():
                                "traffic": read_traffic("decode_conv_step", dinp.name),
                                "alg_bytes_per_launch": int(B_fused), "avg_launch_us": round(f_step, 2)}}}
 
+    # ------------------------------------- multi-layer decode, eager vs graph
+    # A token's step through `layers` layers of the fused, gated decode step
+    # (each layer its own taps, gates, state pool and window), issued call by
+    # call from Python, and as one captured HIP graph replayed per token.
+    def decode_graph_figures(batch, layers=8, tokens=50):
+        hv, cc_ = dsh.num_v_heads, dsh.conv_channels
+        r = np.random.default_rng(batch)
+        ly = []
+        for _ in range(layers):
+            ly.append(dict(
+                w=torch.from_numpy((0.5 * r.normal(size=(cc_, 4))).astype(np.float32)).to(dev),
+                A=torch.from_numpy(r.uniform(-1, 1.5, size=hv).astype(np.float32)).to(dev),
+                D=torch.from_numpy((0.5 * r.normal(size=hv)).astype(np.float32)).to(dev),
+                S=torch.from_numpy((0.02 * r.normal(size=(batch, hv, dsh.head_dim_k, dsh.head_dim_v)))
+                                   .astype(np.float32)).to(dev),
+                W=torch.zeros((batch, 3, cc_), dtype=torch.bfloat16, device=dev),
+                x=torch.from_numpy(r.normal(size=(batch, cc_)).astype(np.float32)).to(torch.bfloat16).to(dev),
+                ab=torch.from_numpy(r.normal(size=(batch, 2 * hv)).astype(np.float32)).to(torch.bfloat16).to(dev),
+                o=torch.empty((batch, hv, dsh.head_dim_v), dtype=torch.bfloat16, device=dev)))
+
+        def bind():
+            return ([gdn.DecodeConv(l_["x"], l_["w"], num_qk_heads=dsh.num_qk_heads, num_v_heads=hv,
+                                    head_dim_k=dsh.head_dim_k, head_dim_v=dsh.head_dim_v, num_slots=batch)
+                     for l_ in ly],
+                    [gdn.gate_inputs(l_["ab"][:, :hv], l_["ab"][:, hv:], l_["A"], l_["D"]) for l_ in ly])
+
+        def token(steps, gates):
+            for i, l_ in enumerate(ly):
+                gdn.decode_conv_gated_step(steps[i], l_["x"], gates[i], l_["S"], l_["W"], l_["o"])
+
+        steps_e, gates_e = bind()
+        for _ in range(5):
+            token(steps_e, gates_e)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(tokens):
+            token(steps_e, gates_e)
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / tokens
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            steps_w, gates_w = bind()
+            token(steps_w, gates_w)
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            steps_g, gates_g = bind()
+            token(steps_g, gates_g)
+        for _ in range(5):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(tokens):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = (time.perf_counter() - t0) / tokens
+        del graph, ly
+        return {"batch": batch, "layers": layers, "tokens": tokens, "eager_us_per_token": round(eager * 1e6, 1),
+                "graph_us_per_token": round(replay * 1e6, 1),
+                "graph_tokens_per_s": round(batch / replay, 1)}
+
+    decode["multilayer_graph"] = [decode_graph_figures(1), decode_graph_figures(Bd)]
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
