@@ -264,3 +264,25 @@ def test_gated_calls_reject_before_any_gpu_call(g):
 
     assert dec(None) == 1 and dec(gates(b=0)) == 1
     assert dec(gates(), slots=2) == 1         # fewer slots than sequences
+
+
+def test_struct_layouts_match_the_header(g, tmp_path):
+    """The binding's ctypes structs have the C header's size and field offsets
+    (compiled with the host C compiler; no GPU involved)."""
+    structs = {"gdn_dims": g.GdnDims, "gdn_gate_inputs": g.GdnGateInputs}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "gdn.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
