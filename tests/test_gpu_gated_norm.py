@@ -27,7 +27,7 @@ def _row_err(y, ref):
 
 
 @pytest.mark.parametrize("dtype,n,h,d", [("bf16", 4096, 32, 128), ("bf16", 37, 3, 64), ("f32", 300, 5, 128),
-                                         ("f32", 1, 1, 64)])
+                                         ("f32", 1, 1, 64), ("bf16", 1001, 7, 128)])
 def test_gated_norm_matches_oracle(G, orc, dtype, n, h, d):
     note(f"gated norm dtype={dtype} n={n} h={h} d={d}")
     r = np.random.default_rng(n + h + d)

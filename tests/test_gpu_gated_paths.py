@@ -25,10 +25,16 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
 
-@pytest.mark.parametrize("which", ["4k-bf16", "varlen-f32"])
+@pytest.mark.parametrize("which", ["4k-bf16", "varlen-f32", "varlen-bf16-c32"])
 def test_gated_prefill_equals_gating_then_prefill(G, which):
     if which == "4k-bf16":
         inp, dtype, cu, chunk = synth.prefill_4k_bf16(), "bf16", None, 64
+    elif which == "varlen-bf16-c32":
+        # the segment-parallel carry over several sequences, chunk 32, ragged tails
+        lens = [5, 300, 1031, 64]
+        inp = synth.make_prefill(13, synth.QWEN35_4B, lens, "bf16", name="gated-varlen-bf16")
+        dtype, chunk = "bf16", 32
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
     else:
         inp = synth.make_prefill(12, synth.TINY, [1, 70, 33, 128], "f32", name="gated-varlen")
         dtype, chunk = "f32", 16
@@ -102,3 +108,35 @@ def test_gated_decode_equals_gating_then_decode(G):
         assert np.array_equal(_bits(o_a), _bits(o_b)), f"o differs at step {i}"
         assert np.array_equal(_bits(S_a), _bits(S_b)), f"state differs at step {i}"
         assert np.array_equal(_bits(W_a), _bits(W_b)), f"window differs at step {i}"
+
+
+def test_gated_decode_tiled_heads_group4(G, orc):
+    """The gated, fused decode step with tiled head order and four v-heads per
+    q/k head, against gating + conv step + plain decode step in fp64."""
+    hk, hv, d, B, W = 2, 8, 64, 3, 4
+    cc = 2 * hk * d + hv * d
+    r = np.random.default_rng(44)
+    x = r.normal(size=(B, cc)).astype(np.float32)
+    w = (0.5 * r.normal(size=(cc, W))).astype(np.float32)
+    win = r.normal(size=(B, W - 1, cc)).astype(np.float32)
+    S0 = (0.05 * r.normal(size=(B, hv, d, d))).astype(np.float32)
+    ab, A_log, dt_bias = synth.gating_inputs(45, B, hv, "f32")
+    S = torch.from_numpy(S0).cuda()
+    Wd = to_dev(win)
+    step = G.DecodeConv(to_dev(x), to_dev(w), num_qk_heads=hk, num_v_heads=hv, head_dim_k=d, head_dim_v=d,
+                        num_slots=B, heads_tiled=True)
+    abd = to_dev(ab)
+    o = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
+    G.decode_conv_gated_step(step, to_dev(x), G.gate_inputs(abd[:, :hv], abd[:, hv:], to_dev(A_log), to_dev(dt_bias)),
+                             S, Wd, o)
+    torch.cuda.synchronize()
+    g, beta = orc.gating(ab[:, :hv], ab[:, hv:], A_log, dt_bias)
+    cu1 = np.arange(B + 1).astype(np.int32)
+    y = orc.conv1d_f32(x, w, cu1, window=win)
+    q, k, v = y[:, :hk * d].reshape(B, hk, d), y[:, hk * d:2 * hk * d].reshape(B, hk, d), y[:, 2 * hk * d:].reshape(B, hv, d)
+    o_ref, S_ref = orc.decode_step(q, k, v, g, beta, S0, heads_tiled=True)
+    eo = float(np.max(np.abs(o.cpu().numpy() - o_ref)) / np.max(np.abs(o_ref)))
+    es = float(np.max(np.abs(S.cpu().numpy() - S_ref)) / np.max(np.abs(S_ref)))
+    note(f"  gated tiled decode: o err {eo:.2e}, S err {es:.2e}")
+    assert eo <= 2e-3 and es <= 2e-3
+    assert np.array_equal(Wd[:, -1].cpu().numpy(), x)
