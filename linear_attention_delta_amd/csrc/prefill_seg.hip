@@ -554,19 +554,23 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
 // ----------------------------------------------------------------- combine
 // S_start[p+1] = Phi_p S_start[p] + B_p for p = 1 .. nseg-2, in place over
 // B_p.  The chain is separable by state columns: one workgroup per
-// (sequence, v-head, CW 16-column tiles), CW + LW waves:
-//  - waves 0..CW-1 each own one 16-column tile of S (all rows) in
-//    accumulators, so S feeds the matrix cores straight from registers; they
-//    only store;
+// (sequence, v-head, CW 16-column tiles), CW RS + LW waves:
+//  - waves 0..CW RS-1 hold one 16-column tile of S (all rows) in registers,
+//    so S feeds the matrix cores straight from them; RS waves share a tile
+//    by rows of the product, each computing and storing its NDT / RS row
+//    tiles and passing them to the others through LDS (parity-double-
+//    buffered, ordered by the step's barrier); they only store;
 //  - waves CW.. only load: Phi_p and the B_p columns, NS steps ahead in NS
 //    register sets, into an NS-slot LDS ring.
 // Keeping loads and stores in different waves means no wait for a load ever
 // has to wait for a store to be acknowledged.  The column groups of one
 // v-head get the same blockIdx % 8, i.e. the same XCD, and share its L2 for
 // the transitions.
-template <int DK, int DV, int CW, int LW, int NS>
-__global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
+template <int DK, int DV, int CW, int RS, int LW, int NS>
+__global__ void __launch_bounds__(64 * (CW * RS + LW)) k_seg_combine(ScanArgs a) {
   constexpr int NDT = DK / 16, KS = DK / 32;
+  constexpr int UPR = NDT / RS;                             // row tiles per compute wave
+  static_assert(UPR * RS == NDT, "row tiles must split over the row shares");
   constexpr int NG = DV / (16 * CW);                        // column groups per v-head
   constexpr int LT = 64 * LW;                               // loader threads
   constexpr int PV = DK * DK / 8 / LT;                      // 16-byte words of Phi per loader thread
@@ -574,6 +578,8 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   static_assert(PV * LT * 8 == DK * DK && BV * LT == NDT * CW * 64, "shape");
   __shared__ u32x4 phl[NS][DK * DK / 8];
   __shared__ f32x4 bl[NS][NDT * CW * 64];                   // [u][tile][lane]
+  constexpr int SXN = RS > 1 ? 2 * CW * NDT * 64 : 1;
+  __shared__ f32x4 sx[SXN];                                 // [parity][tile][u][lane]: rows passed between shares
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
   const int grp = m8 % NG;                                  // column group
@@ -593,8 +599,8 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   const int last = nseg - 2;  // steps p = 1 .. last
   auto sptr = [&](int p) { return a.seg_state + ((long)(sbase + p) * a.hv + h) * DK * DV; };
 
-  if (wave >= CW) {
-    const int lt = tid - 64 * CW;
+  if (wave >= CW * RS) {
+    const int lt = tid - 64 * CW * RS;
     struct Set {
       u32x4 pf[PV];
       f32x4 bf[BV];
@@ -636,7 +642,8 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
     return;
   }
 
-  const int jt = CW * grp + wave;  // this wave's column tile
+  const int ct = wave / RS, rs = wave % RS;  // column tile, row share
+  const int jt = CW * grp + ct;
   f32x4 S[NDT];
   {
     const float* s1 = sptr(1);
@@ -646,21 +653,31 @@ __global__ void __launch_bounds__(64 * (CW + LW)) k_seg_combine(ScanArgs a) {
   for (int p = 1; p <= last; p++) {
     lds_barrier();
     const int b = p % NS;
-    f32x4 acc[NDT];
+    if constexpr (RS > 1) {
+      // the other shares' rows of S_p, written at step p - 1
+      if (p > 1) {
 #pragma unroll
-    for (int u = 0; u < NDT; u++) acc[u] = bl[b][(u * CW + wave) * 64 + lane];
+        for (int u = 0; u < NDT; u++)
+          if (u / UPR != rs) S[u] = sx[(((p & 1) * CW + ct) * NDT + u) * 64 + lane];
+      }
+    }
+    f32x4 acc[UPR];
+#pragma unroll
+    for (int i = 0; i < UPR; i++) acc[i] = bl[b][((rs * UPR + i) * CW + ct) * 64 + lane];
 #pragma unroll
     for (int m = 0; m < KS; m++) {
       const bf16x8 zb = frag_acc(S[2 * m], S[2 * m + 1]);
 #pragma unroll
-      for (int u = 0; u < NDT; u++)
-        acc[u] = mfma16(__builtin_bit_cast(bf16x8, phl[b][(u * KS + m) * 64 + lane]), zb, acc[u]);
+      for (int i = 0; i < UPR; i++)
+        acc[i] = mfma16(__builtin_bit_cast(bf16x8, phl[b][((rs * UPR + i) * KS + m) * 64 + lane]), zb, acc[i]);
     }
     float* dst = sptr(p + 1);
 #pragma unroll
-    for (int u = 0; u < NDT; u++) {
-      S[u] = acc[u];
-      *reinterpret_cast<f32x4*>(dst + state_frag<DV>(u, jt, lane)) = acc[u];
+    for (int i = 0; i < UPR; i++) {
+      const int u = rs * UPR + i;
+      S[u] = acc[i];
+      *reinterpret_cast<f32x4*>(dst + state_frag<DV>(u, jt, lane)) = acc[i];
+      if constexpr (RS > 1) sx[((((p + 1) & 1) * CW + ct) * NDT + u) * 64 + lane] = acc[i];
     }
   }
 }
@@ -768,6 +785,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
 // State-column tiles (16 columns each) per combine workgroup, and the depth
 // of its load ring (steps in flight ahead of the chain).
 constexpr int kCombineWaves = 1;
+constexpr int kCombineRowShares = 4;  // compute waves per column tile (2: 8.55 us, 8: 8.8 us, 4: 8.3 us)
 constexpr int kCombineSlots = 2;
 // Carry waves of pass 2 (each owns d_v / (16 kPass2CarryWaves) column tiles).
 constexpr int kPass2CarryWaves = 4;
@@ -783,9 +801,10 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   {
     constexpr int CW = kCombineWaves, LW = 4, NG = DV / (16 * CW);
+    constexpr int RS = kCombineRowShares <= DK / 16 ? kCombineRowShares : DK / 16;
     const int units = a.num_seqs * a.hv;
-    hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, LW, kCombineSlots>), dim3(8 * ((units + 7) / 8) * NG),
-                       dim3(64 * (CW + LW)), 0, s, a);
+    hipLaunchKernelGGL((k_seg_combine<DK, DV, CW, RS, LW, kCombineSlots>), dim3(8 * ((units + 7) / 8) * NG),
+                       dim3(64 * (CW * RS + LW)), 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   constexpr int NCW = kPass2CarryWaves * 16 <= DV ? kPass2CarryWaves : DV / 16;
