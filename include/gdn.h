@@ -116,14 +116,40 @@ const char *gdn_last_error(void);
 const char *gdn_version(void);
 
 /*
- * Host-only check of a problem description, no GPU needed: the same shape
- * rules the entry points apply before queuing anything (pointer and
- * workspace checks happen in the entry points).  op: 0 = prefill, 1 = decode.
+ * Host-only check of a problem description, no GPU needed: the shape rules
+ * the entry points apply before queuing anything.  The shapes are those of
+ * the layer as the oxydllm notes describe it ("New Features": a per-head
+ * d_k x d_v fp32 memory, grouped q/k heads shared by several v-heads, in
+ * repeat-interleave or tiled order); head dims 64 and 128 and chunks of 16,
+ * 32 or 64 are the ones this library implements.  op: 0 = prefill,
+ * 1 = decode.  Returns GDN_OK or the status the entry points would return.
  */
 gdn_status gdn_validate_dims(const gdn_dims *d, int32_t op);
 
 /*
- * Causal depthwise conv1d (+ optional SiLU) over packed sequences.
+ * Host-only check of a whole call, no GPU needed: exactly the checks that
+ * gdn_prefill_chunked (op 0) or gdn_decode_step (op 1) run before queuing
+ * anything -- shapes, NULL pointers, 16-byte alignment, state overlap and
+ * workspace size -- with the pointers only compared, never dereferenced.
+ * ptrs holds the call's pointer arguments in the order of its signature:
+ *   op 0: q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace
+ *         (n_ptrs = 10); extent = the workspace size in bytes;
+ *   op 1: q, k, v, g, beta, state, state_slots, o (n_ptrs = 8);
+ *         extent = num_slots.
+ * Returns what the entry point would return for these arguments had the
+ * GPU accepted the launch (GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED
+ * or GDN_ERR_WORKSPACE); gdn_last_error() says why.
+ */
+gdn_status gdn_validate(const gdn_dims *d, int32_t op, const void *const *ptrs, int32_t n_ptrs,
+                        int64_t extent);
+
+/*
+ * Causal depthwise conv1d (+ optional SiLU) over packed sequences: the short
+ * convolution that produces the layer's q, k and v (Vallmo.jl README,
+ * "What's here": causal conv1d is one of the hybrid layer's kernels; PicoLM
+ * fork changelog, "GPU: Device-Native Pipeline Rewrite": conv1d runs as its
+ * own device kernel), with the per-sequence causal-conv window the oxydllm
+ * notes ("New Features") keep beside the recurrent memory.
  *
  * For sequence i and channel c, with x_i its tokens and w[c][0..W-1]:
  *     y[t][c] = act( bias[c] + sum_{j=0}^{W-1} w[c][j] * xx[t - (W-1) + j][c] )

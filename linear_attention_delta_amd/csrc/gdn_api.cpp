@@ -243,6 +243,18 @@ void set_gates(gdn::ScanArgs& a, const gdn_gate_inputs* G) {
   a.dt_bias = G->dt_bias;
 }
 
+// state_out may be state_in itself (in place) but must not partially overlap it
+gdn_status check_state_overlap(const gdn_dims* d, const float* state_in, const float* state_out) {
+  if (state_in && state_out && state_in != state_out) {
+    const size_t sbytes = (size_t)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v * 4;
+    const char* a0 = reinterpret_cast<const char*>(state_in);
+    const char* b0 = reinterpret_cast<const char*>(state_out);
+    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
+      return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
+  }
+  return GDN_OK;
+}
+
 gdn_status check_workspace(const gdn_dims* d, const void* ws, size_t ws_bytes) {
   const WsLayout L = ws_layout(d);
   if (L.total > 0 && !ws) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
@@ -304,6 +316,7 @@ const char* gdn_last_error(void) { return g_last_error.c_str(); }
 const char* gdn_version(void) { return "0.1.0"; }
 
 gdn_status gdn_validate_dims(const gdn_dims* d, int32_t op) { return check_dims(d, op); }
+
 
 gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen, const int32_t* cu_seqlens,
                       int32_t channels, int32_t width, int32_t dtype, const void* x, int64_t stride_x,
@@ -393,13 +406,7 @@ static gdn_status scan_impl(const gdn_dims* d, const void* q, const void* k, con
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
     return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
-  if (state_in && state_out && state_in != state_out) {
-    const size_t sbytes = (size_t)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v * 4;
-    const char* a0 = reinterpret_cast<const char*>(state_in);
-    const char* b0 = reinterpret_cast<const char*>(state_out);
-    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
-      return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
-  }
+  if ((st = check_state_overlap(d, state_in, state_out)) != GDN_OK) return st;
   gdn::ScanArgs a = make_args(d);
   a.q = q;
   a.k = k;
@@ -422,17 +429,26 @@ gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, con
   return scan_impl(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream, true);
 }
 
-gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
-                               float* state_out, void* workspace, size_t ws_bytes, void* stream) {
+// Every check of gdn_prefill_chunked (both halves), host only.
+static gdn_status validate_prefill(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* state_in, const int32_t* cu_seqlens,
+                                   const void* o, const float* state_out, const void* workspace, size_t ws_bytes) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
   if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true)) != GDN_OK) return st;
   if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
-  // validate the scan half fully before queuing the prepare half
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
     return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
+  return check_state_overlap(d, state_in, state_out);
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
+                               float* state_out, void* workspace, size_t ws_bytes, void* stream) {
+  // validate the scan half fully before queuing the prepare half
+  gdn_status st = validate_prefill(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes);
+  if (st != GDN_OK) return st;
   if ((st = gdn_prefill_prepare(d, q, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
   return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
 }
@@ -530,13 +546,7 @@ static gdn_status conv_chunked_impl(const gdn_dims* d, const gdn_gate_inputs* ga
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
     return fail(GDN_ERR_INVALID_ARG, "states must be 16-byte aligned");
-  if (state_in && state_out && state_in != state_out) {
-    const size_t sbytes = (size_t)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v * 4;
-    const char* a0 = reinterpret_cast<const char*>(state_in);
-    const char* b0 = reinterpret_cast<const char*>(state_out);
-    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
-      return fail(GDN_ERR_INVALID_ARG, "state_out may alias state_in exactly but not partially overlap it");
-  }
+  if ((st = check_state_overlap(d, state_in, state_out)) != GDN_OK) return st;
   if ((st = conv_prepare_impl(d, gates, conv_width, x, stride_x, conv_weight, conv_bias, conv_state, g, beta,
                               cu_seqlens, y, stride_y, workspace, ws_bytes, stream)) != GDN_OK)
     return st;
@@ -568,19 +578,28 @@ gdn_status gdn_prefill_conv_gated(const gdn_dims* d, const gdn_gate_inputs* gate
                            state_in, cu_seqlens, y, stride_y, o, state_out, workspace, ws_bytes, stream);
 }
 
-gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, float* state, int32_t num_slots, const int32_t* state_slots, void* o,
-                           void* stream) {
+// Every check of gdn_decode_step, host only.
+static gdn_status validate_decode(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const float* state, int64_t num_slots,
+                                  const int32_t* state_slots, const void* o) {
   gdn_status st = check_dims(d, 1);
   if (st != GDN_OK) return st;
   if ((st = check_scan_ptrs(d, q, k, v, g, beta, nullptr, true)) != GDN_OK) return st;
   if (!o || !aligned(o, 16)) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
   if (!state || !aligned(state, 16)) return fail(GDN_ERR_INVALID_ARG, "state must be non-NULL and 16-byte aligned");
-  if (num_slots < 1) return fail(GDN_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (num_slots < 1 || num_slots > INT32_MAX) return fail(GDN_ERR_INVALID_ARG, "num_slots must be in [1, 2^31)");
   if (!state_slots && num_slots < d->num_seqs)
-    return fail(GDN_ERR_INVALID_ARG, "without state_slots, num_slots (%d) must be >= num_seqs (%d)", num_slots,
-                d->num_seqs);
+    return fail(GDN_ERR_INVALID_ARG, "without state_slots, num_slots (%lld) must be >= num_seqs (%d)",
+                (long long)num_slots, d->num_seqs);
   if (state_slots && !aligned(state_slots, 4)) return fail(GDN_ERR_INVALID_ARG, "state_slots must be 4-byte aligned");
+  return GDN_OK;
+}
+
+gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, int32_t num_slots, const int32_t* state_slots, void* o,
+                           void* stream) {
+  gdn_status st = validate_decode(d, q, k, v, g, beta, state, num_slots, state_slots, o);
+  if (st != GDN_OK) return st;
   gdn::ScanArgs a = make_args(d);
   a.q = q;
   a.k = k;
@@ -787,6 +806,24 @@ gdn_status gdn_gating(int32_t total_tokens, int32_t num_heads, int32_t dtype, co
     if ((st = debug_check(s, "beta", beta, (long)total_tokens * num_heads, GDN_F32)) != GDN_OK) return st;
   }
   return ok();
+}
+
+gdn_status gdn_validate(const gdn_dims* d, int32_t op, const void* const* ptrs, int32_t n_ptrs, int64_t extent) {
+  if (op != 0 && op != 1) return fail(GDN_ERR_INVALID_ARG, "op must be 0 (prefill) or 1 (decode)");
+  const int32_t need = op == 0 ? 10 : 8;
+  if (!ptrs || n_ptrs != need)
+    return fail(GDN_ERR_INVALID_ARG, "%s takes %d pointers (got %d)", op == 0 ? "prefill" : "decode", need, n_ptrs);
+  const float* const* fp = reinterpret_cast<const float* const*>(ptrs);
+  gdn_status st;
+  if (op == 0) {
+    if (extent < 0) return fail(GDN_ERR_INVALID_ARG, "workspace bytes must be >= 0");
+    st = validate_prefill(d, ptrs[0], ptrs[1], ptrs[2], fp[3], fp[4], fp[5], reinterpret_cast<const int32_t*>(ptrs[6]),
+                          ptrs[7], fp[8], ptrs[9], (size_t)extent);
+  } else {
+    st = validate_decode(d, ptrs[0], ptrs[1], ptrs[2], fp[3], fp[4], fp[5], extent,
+                         reinterpret_cast<const int32_t*>(ptrs[6]), ptrs[7]);
+  }
+  return st == GDN_OK ? ok() : st;
 }
 
 }  // extern "C"

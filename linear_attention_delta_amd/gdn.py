@@ -25,7 +25,7 @@ OP_DECODE = 1
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_WORKSPACE",
                 4: "GDN_ERR_HIP", 5: "GDN_ERR_NONFINITE"}
 
-EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_conv1d",
+EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_validate", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
             "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
             "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step"]
@@ -66,6 +66,7 @@ def _load():
         "gdn_last_error": ([], ctypes.c_char_p),
         "gdn_version": ([], ctypes.c_char_p),
         "gdn_validate_dims": ([D, i32], i32),
+        "gdn_validate": ([D, i32, ctypes.POINTER(P), i32, i64], i32),
         "gdn_conv1d": ([i32, i32, i32, P, i32, i32, i32, P, i64, P, P, P, i32, P, i64, P], i32),
         "gdn_prefill_workspace_size": ([D], sz),
         "gdn_prefill_chunked": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
@@ -111,6 +112,13 @@ def validate_dims(d: GdnDims, op: int) -> int:
     return int(lib.gdn_validate_dims(ctypes.byref(d), op))
 
 
+def validate(d: GdnDims, op: int, ptrs, extent: int) -> int:
+    """Host-only check of a prefill (op 0) or decode (op 1) call's arguments:
+    ptrs are integer addresses (or None) in the order gdn_validate lists."""
+    arr = (ctypes.c_void_p * len(ptrs))(*[None if p is None else int(p) for p in ptrs])
+    return int(lib.gdn_validate(ctypes.byref(d), op, arr, len(ptrs), int(extent)))
+
+
 # ---- torch helpers (memory and streams only) -----------------------------
 
 def _ptr(t) -> Optional[int]:
@@ -121,6 +129,21 @@ def _stream(stream=None) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _keep_for_stream(stream, *tensors):
+    """Tensors allocated here on the current stream but used by kernels queued
+    on another `stream`: tell torch's caching allocator, so that a block
+    dropped at return (the temporary workspace) is not handed out again
+    before that stream's kernels are done with it."""
+    if stream is None:
+        return
+    import torch
+    if stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _dtype_code(t) -> int:
@@ -156,6 +179,7 @@ def conv1d(x, weight, *, cu_seqlens=None, seqlen=None, num_seqs=None, bias=None,
     _check(lib.gdn_conv1d(n_seq, n_tok, sl, _ptr(cu_seqlens), C, weight.shape[1], _dtype_code(x),
                           _ptr(x), x.stride(0), _ptr(weight), _ptr(bias), _ptr(conv_state),
                           1 if activation else 0, _ptr(out), out.stride(0), _stream(stream)))
+    _keep_for_stream(stream, out)
     return out
 
 
@@ -254,6 +278,7 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, nu
     if state_out is None and want_state:
         state_out = torch.empty((p.dims.num_seqs, hv, q.shape[2], dv), dtype=torch.float32, device=q.device)
     p(q, k, v, g, beta, out, state_in, state_out, stream)
+    _keep_for_stream(stream, p.ws, out, state_out)
     return out, state_out
 
 
@@ -329,6 +354,7 @@ def conv_prefill(x, weight, g, beta, *, num_qk_heads, num_v_heads, head_dim_k, h
     st = torch.empty((p.dims.num_seqs, num_v_heads, head_dim_k, head_dim_v), dtype=torch.float32,
                      device=x.device) if want_state else None
     p(x, y, g, beta, o, state_in, st, conv_state, stream)
+    _keep_for_stream(stream, p.ws, y, o, st)
     return y, o, st
 
 
@@ -364,6 +390,7 @@ def decode_step(q, k, v, g, beta, state, *, state_slots=None, l2norm=True, heads
         out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
     _check(lib.gdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                state.shape[0], _ptr(state_slots), _ptr(out), _stream(stream)))
+    _keep_for_stream(stream, out)
     return out
 
 
@@ -413,6 +440,7 @@ def decode_conv_step(x, weight, g, beta, state, conv_state, *, num_qk_heads, num
     _check(lib.gdn_decode_conv_step(ctypes.byref(d), weight.shape[1], _ptr(x), x.stride(0), _ptr(weight), _ptr(bias),
                                     _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), state.shape[0],
                                     _ptr(state_slots), _ptr(out), _stream(stream)))
+    _keep_for_stream(stream, out)
     return out
 
 
@@ -447,6 +475,7 @@ def gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None, stream=None):
         out = torch.empty((n, h, d), dtype=o.dtype, device=o.device)
     _check(lib.gdn_gated_rmsnorm(n, h, d, _dtype_code(o), _ptr(o), _row_stride(o), _ptr(z), _row_stride(z),
                                  _ptr(weight), float(eps), _ptr(out), _row_stride(out), _stream(stream)))
+    _keep_for_stream(stream, out)
     return out
 
 
@@ -479,7 +508,9 @@ def gating(a, b, A_log, dt_bias, *, g=None, beta=None, stream=None):
         g = torch.empty((n, h), dtype=torch.float32, device=a.device)
     if beta is None:
         beta = torch.empty((n, h), dtype=torch.float32, device=a.device)
-    return Gating(a, b, A_log, dt_bias, stream=stream)(a, b, g, beta)
+    Gating(a, b, A_log, dt_bias, stream=stream)(a, b, g, beta)
+    _keep_for_stream(stream, g, beta)
+    return g, beta
 
 
 def gate_inputs(a, b, A_log, dt_bias) -> GdnGateInputs:

@@ -104,11 +104,14 @@ class Oracle:
         return float(self.lib.gdn_oracle_exp_f32(ctypes.c_float(x)))
 
     def scan(self, q, k, v, g, beta, cu_seqlens=None, *, state0=None, scale=1.0, l2norm=True,
-             heads_tiled=False, n_threads=0, return_threads=False):
+             heads_tiled=False, n_threads=0, return_threads=False, state_out=None):
         """Token-by-token gated delta rule in fp64.
 
         q, k [N][H_k][d_k]; v [N][H_v][d_v]; g, beta [N][H_v]; state0
-        [n_seq][H_v][d_k][d_v] or None.  Returns (o [N][H_v][d_v], S [n_seq][H_v][d_k][d_v])."""
+        [n_seq][H_v][d_k][d_v] or None.  Returns (o [N][H_v][d_v], S [n_seq][H_v][d_k][d_v]).
+        state_out: optional C-contiguous fp64 array of S's shape to write S
+        into; it may be state0 itself (each (sequence, head) slice is read
+        before it is written), which steps a large state without copies."""
         q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
         n_tok, Hk, dk = q.shape
         _, Hv, dv = v.shape
@@ -120,7 +123,14 @@ class Oracle:
         if s0 is not None:
             assert s0.shape == (n_seq, Hv, dk, dv)
         o = np.zeros((n_tok, Hv, dv), dtype=np.float64)
-        S = np.zeros((n_seq, Hv, dk, dv), dtype=np.float64)
+        if state_out is not None:
+            assert state_out.dtype == np.float64 and state_out.flags.c_contiguous
+            assert state_out.shape == (n_seq, Hv, dk, dv)
+            if state0 is not None and np.shares_memory(state_out, state0):
+                assert s0 is state0, "state_out may alias state0 only when state0 is contiguous fp64"
+            S = state_out
+        else:
+            S = np.zeros((n_seq, Hv, dk, dv), dtype=np.float64)
         flags = (L2NORM if l2norm else 0) | (HEADS_TILED if heads_tiled else 0)
         nt = self.lib.gdn_oracle_scan(n_seq, _ptr(cu), Hk, Hv, dk, dv, float(scale), flags,
                                       _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
@@ -151,14 +161,15 @@ class Oracle:
         return g, beta
 
     def decode_step(self, q, k, v, g, beta, state, *, scale=1.0, l2norm=True, heads_tiled=False,
-                    n_threads=0):
+                    n_threads=0, in_place=False):
         """One recurrent step for B sequences (one token each): q, k [B][H_k][d_k],
         v [B][H_v][d_v], g, beta [B][H_v], state [B][H_v][d_k][d_v].
-        Returns (o [B][H_v][d_v], new state)."""
+        Returns (o [B][H_v][d_v], new state); with in_place the new state is
+        written over `state` (C-contiguous fp64) and that array is returned."""
         B = q.shape[0]
         cu = np.arange(B + 1, dtype=np.int32)
         return self.scan(q, k, v, g, beta, cu, state0=state, scale=scale, l2norm=l2norm,
-                         heads_tiled=heads_tiled, n_threads=n_threads)
+                         heads_tiled=heads_tiled, n_threads=n_threads, state_out=state if in_place else None)
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -12,6 +12,8 @@ import sys
 
 import numpy as np
 
+from linear_attention_delta_amd import synth
+
 TOL = {"f32": 2e-3, "bf16": 2e-2}
 
 
@@ -46,28 +48,45 @@ def to_np(t) -> np.ndarray:
 
 def rel_err_slices(x: np.ndarray, ref: np.ndarray, cu_seqlens=None) -> float:
     """x, ref: o [N_tok][H][d] (slices by sequence and head) or S
-    [N][H][dk][dv] (slices by leading two axes)."""
-    x = np.asarray(x, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    [N][H][dk][dv] (slices by leading two axes).  Vectorised over heads (and
+    over sequences when they all have one length), so every (sequence, head)
+    slice of a large workload is checked in seconds."""
+    x = np.asarray(x)
+    ref = np.asarray(ref)
     assert x.shape == ref.shape, (x.shape, ref.shape)
-    worst = 0.0
+
+    def ratio(num, den):
+        return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num))) if num.size else 0.0
+
     if x.ndim == 4:
-        for s in range(x.shape[0]):
-            for h in range(x.shape[1]):
-                den = np.max(np.abs(ref[s, h]))
-                num = np.max(np.abs(x[s, h] - ref[s, h]))
-                worst = max(worst, num / den if den > 0 else num)
-        return worst
-    cu = [0, x.shape[0]] if cu_seqlens is None else list(cu_seqlens)
+        d = np.abs(x.astype(np.float64) - ref)
+        return ratio(np.max(d, axis=(2, 3)), np.max(np.abs(ref), axis=(2, 3)).astype(np.float64))
+    cu = np.array([0, x.shape[0]]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    lens = np.diff(cu)
+    if lens.size and np.all(lens == lens[0]) and lens[0] > 0 and cu[0] == 0:
+        n, L = lens.size, int(lens[0])
+        xs = x[:n * L].reshape(n, L, *x.shape[1:])
+        rs = ref[:n * L].reshape(n, L, *ref.shape[1:])
+        d = np.abs(xs.astype(np.float64) - rs)
+        return ratio(np.max(d, axis=(1, 3)), np.max(np.abs(rs), axis=(1, 3)).astype(np.float64))
+    worst = 0.0
     for i in range(len(cu) - 1):
         a, b = int(cu[i]), int(cu[i + 1])
         if a == b:
             continue
-        for h in range(x.shape[1]):
-            den = np.max(np.abs(ref[a:b, h]))
-            num = np.max(np.abs(x[a:b, h] - ref[a:b, h]))
-            worst = max(worst, num / den if den > 0 else num)
+        d = np.abs(x[a:b].astype(np.float64) - ref[a:b])
+        worst = max(worst, ratio(np.max(d, axis=(0, 2)), np.max(np.abs(ref[a:b]), axis=(0, 2)).astype(np.float64)))
     return worst
+
+
+def oracle_scan_all(orc, inp, y, *, state0="inp", heads_tiled=False, scale=None, l2norm=True):
+    """The oracle's token scan over every (sequence, v-head) of a workload in
+    one threaded call, on the q/k/v column blocks of the conv output y.
+    Returns (o [N_tok][H_v][d_v], S [N][H_v][d_k][d_v]) in fp64."""
+    q, k, v = synth.split_qkv(y, inp.shape)
+    s0 = inp.state0 if isinstance(state0, str) else state0
+    return orc.scan(q, k, v, inp.g, inp.beta, inp.cu_seqlens, state0=s0,
+                    scale=inp.scale if scale is None else scale, l2norm=l2norm, heads_tiled=heads_tiled)
 
 
 def conv_inputs(orc, inp, *, gpu_dtype=None):

@@ -286,3 +286,52 @@ def test_struct_layouts_match_the_header(g, tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for field, _ in py._fields_:
             assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
+
+
+def test_partial_state_overlap_rejected_before_any_gpu_call(g):
+    """gdn_prefill_chunked checks the state_in / state_out overlap before it
+    queues the prepare: on this GPU-less host, a check that ran after a launch
+    would surface as GDN_ERR_HIP instead."""
+    L = g.lib
+    d = _dims(g)
+    ws = g.workspace_size(d)
+    sbytes = 32 * 128 * 128 * 4
+    si = 1 << 26
+    for so in (si + 16, si + sbytes - 16, si - sbytes + 16):   # partial overlaps
+        st = L.gdn_prefill_chunked(ctypes.byref(d), 16, 16, 16, 16, 16, si, None, 16, so, 256, ws, None)
+        assert st == 1 and "overlap" in g.last_error(), (so, st, g.last_error())
+
+
+def test_validate_whole_calls(g):
+    """gdn_validate runs the entry points' host checks on a call's pointers."""
+    d = _dims(g)
+    ws = g.workspace_size(d)
+    good = [16, 32, 48, 64, 80, 4096, None, 96, 4096, 256]   # in-place state
+    assert g.validate(d, g.OP_PREFILL, good, ws) == g.GDN_OK, g.last_error()
+    bad_cases = [
+        (dict(i=0, v=None), 1), (dict(i=7, v=None), 1), (dict(i=2, v=40), 1),     # q NULL, o NULL, v misaligned
+        (dict(i=8, v=4096 + 32), 1), (dict(i=9, v=None), 3), (dict(i=9, v=128), 3),  # overlap, no / misaligned ws
+        (dict(i=3, v=18), 1),                                                      # g misaligned
+    ]
+    for case, code in bad_cases:
+        p = list(good)
+        p[case["i"]] = case["v"]
+        assert g.validate(d, g.OP_PREFILL, p, ws) == code, (case, g.last_error())
+    assert g.validate(d, g.OP_PREFILL, good, ws - 256) == 3
+    assert g.validate(d, g.OP_PREFILL, good[:9], ws) == 1            # wrong pointer count
+    vd = _dims(g, seqlen=0, total_tokens=100, num_seqs=3)
+    assert g.validate(vd, g.OP_PREFILL, good, g.workspace_size(vd)) == 1   # varlen without cu_seqlens
+    p = list(good)
+    p[6] = 512
+    assert g.validate(vd, g.OP_PREFILL, p, g.workspace_size(vd)) == g.GDN_OK, g.last_error()
+    dd = _dims(g, num_seqs=64, total_tokens=64, seqlen=1)
+    dgood = [16, 32, 48, 64, 80, 4096, None, 96]
+    assert g.validate(dd, g.OP_DECODE, dgood, 64) == g.GDN_OK, g.last_error()
+    assert g.validate(dd, g.OP_DECODE, dgood, 63) == 1               # fewer slots than sequences
+    p = list(dgood)
+    p[6] = 1024
+    assert g.validate(dd, g.OP_DECODE, p, 8) == g.GDN_OK             # slot indices given
+    p[6] = 1026
+    assert g.validate(dd, g.OP_DECODE, p, 8) == 1                    # misaligned slot array
+    assert g.validate(dd, g.OP_DECODE, dgood[:7], 64) == 1
+    assert g.validate(dd, 2, dgood, 64) == 1

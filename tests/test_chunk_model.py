@@ -59,3 +59,53 @@ def test_tiny_workload_through_chunk_model(orc):
     o_ref, S_ref = orc.scan(q, k, v, inp.g, inp.beta, inp.cu_seqlens)
     o, S = chunk_model.chunked_scan(q, k, v, inp.g, inp.beta, inp.cu_seqlens, chunk=64)
     assert _rel(o, o_ref) < 1e-11 and _rel(S, S_ref) < 1e-11
+
+
+@pytest.mark.parametrize("chunk,seg_len", [(64, 1), (32, 2), (16, 3), (64, 8)])
+def test_segment_form_equals_token_recurrence(orc, chunk, seg_len):
+    """The segment-parallel carry (pass 1 -> chained starts -> pass 2) is the
+    chunk loop reassociated: exact in fp64 against the oracle, on ragged
+    sequences with initial states (one, several and partial segments)."""
+    r = np.random.default_rng(100 + chunk + seg_len)
+    lens = [1, 200, 64 * seg_len, 33, 0, 700]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, Hk, Hv, dk, dv = int(cu[-1]), 1, 2, 16, 8
+    q = r.normal(size=(T, Hk, dk)); k = r.normal(size=(T, Hk, dk)); v = r.normal(size=(T, Hv, dv))
+    g = -np.logaddexp(0, r.normal(size=(T, Hv))) * 0.5
+    beta = 1 / (1 + np.exp(-r.normal(size=(T, Hv))))
+    S0 = r.normal(size=(len(lens), Hv, dk, dv)) * 0.1
+    o_ref, S_ref = orc.scan(q, k, v, g, beta, cu, state0=S0, scale=0.7)
+    o, S = chunk_model.segmented_scan(q, k, v, g, beta, cu, state0=S0, chunk=chunk, seg_len=seg_len, scale=0.7)
+    assert _rel(o, o_ref) < 1e-10 and _rel(S, S_ref) < 1e-10
+
+
+def _bf16_layer(T, seed):
+    """One bf16 sequence with the 4096-token layer's head shapes (one q/k
+    head, two v-heads) and its conv + SiLU inputs, as the kernels see them."""
+    sh = synth.LayerShape(1, 2, 128, 128)
+    inp = synth.make_prefill(seed, sh, [T], "bf16")
+    bits = __import__("oracle").default().conv1d_f32(inp.x, inp.conv_w, inp.cu_seqlens, out_bf16=True)
+    y = synth.bf16_bits_to_f32(bits)
+    return inp, synth.split_qkv(y, sh)
+
+
+@pytest.mark.slow
+def test_segment_bf16_error_growth(orc):
+    """The bf16 rounding of the segment path, modelled on the CPU: the worst
+    per-head error of o and of the final state against the fp64 oracle, for
+    segments of 8 to 64 chunks (the lengths the library picks for one
+    sequence of 4096 to 32768 tokens).  Each stays well inside the bf16
+    bound of 2e-2, and a longer segment does not make it grow by more than
+    a small factor over the 8-chunk segments of the 4096-token layer."""
+    from tests.gpu_util import rel_err_slices
+    errs = {}
+    for T, L in ((4096, 8), (8192, 16), (16384, 32), (32768, 64)):
+        inp, (q, k, v) = _bf16_layer(T, 500 + L)
+        o_ref, S_ref = orc.scan(q, k, v, inp.g, inp.beta)
+        o, S = chunk_model.segmented_scan(q, k, v, inp.g, inp.beta, chunk=64, seg_len=L, bf16=True)
+        errs[(T, L)] = (rel_err_slices(o, o_ref), rel_err_slices(S, S_ref))
+        print(f"T={T} seg_len={L}: o err {errs[(T, L)][0]:.2e}  S err {errs[(T, L)][1]:.2e}", flush=True)
+    base = max(errs[(4096, 8)])
+    for key, (eo, es) in errs.items():
+        assert eo <= 1e-2 and es <= 1e-2, key
+        assert max(eo, es) <= 3.0 * base, key

@@ -83,70 +83,87 @@ def test_decode_state_slots(G, orc):
         assert np.array_equal(after[s], before[s])
 
 
-def _decode_pipeline_oracle(orc, inp, steps, seqs, keep=()):
-    """conv step + recurrent step for `steps` steps on the sequences `seqs`
-    (all heads), in fp64 with the fp32 conv; returns per-step o and the
-    states after the steps listed in `keep`."""
-    sh = inp.shape
-    win = inp.conv_state0[seqs].astype(np.float32)
-    S = inp.state0[seqs].astype(np.float64)
-    cu1 = np.arange(len(seqs) + 1).astype(np.int32)
-    outs = []
-    kept = {}
-    for i in range(steps):
-        p = i % inp.pool
-        xt = inp.x[p][seqs]
-        bits = orc.conv1d_f32(xt, inp.conv_w, cu1, window=win, out_bf16=True)
+class DecodePipelineOracle:
+    """conv step + recurrent step of the decode workload, one step at a time,
+    in fp64 with the fp32 conv (q, k, v rounded to bf16 exactly as the GPU's
+    conv stores them), on the sequences `seqs` (all heads).  The fp64 state
+    is stepped in place."""
+
+    def __init__(self, orc, inp, seqs):
+        self.orc, self.inp, self.seqs = orc, inp, np.asarray(seqs)
+        self.win = inp.conv_state0[self.seqs].astype(np.float32)
+        self.S = np.ascontiguousarray(inp.state0[self.seqs], dtype=np.float64)
+        self.cu1 = np.arange(len(self.seqs) + 1).astype(np.int32)
+        self.i = 0
+
+    def step(self):
+        inp, orc = self.inp, self.orc
+        p = self.i % inp.pool
+        xt = inp.x[p][self.seqs]
+        bits = orc.conv1d_f32(xt, inp.conv_w, self.cu1, window=self.win, out_bf16=True)
         y = (bits.astype(np.uint32) << 16).view(np.float32)
-        _, win = orc.conv1d(xt, inp.conv_w, cu1, window=win)
-        win = win.astype(np.float32)
-        q, k, v = synth.split_qkv(y, sh)
-        o, S = orc.decode_step(q, k, v, inp.g[p][seqs], inp.beta[p][seqs], S)
-        outs.append(o)
-        if i + 1 in keep:
-            kept[i + 1] = S.copy()
-    return outs, kept
+        _, win = orc.conv1d(xt, inp.conv_w, self.cu1, window=self.win)
+        self.win = win.astype(np.float32)
+        q, k, v = synth.split_qkv(y, inp.shape)
+        o, _ = orc.decode_step(q, k, v, inp.g[p][self.seqs], inp.beta[p][self.seqs], self.S, in_place=True)
+        self.i += 1
+        return o
 
 
 def test_decode_b64_1000_steps(G, orc):
-    """The 64-sequence Qwen3.5-4B-shaped decode workload: conv step + decode
-    step per token, 1000 steps cycling 16 input sets.  o is checked every
-    step and S at steps 1, 16 and 1000 on a sample of sequences (all heads)."""
+    """The 64-sequence Qwen3.5-4B-shaped decode workload for 1000 steps
+    (cycling 16 input sets), through both decode paths: conv step + decode
+    step (two calls), and the fused gdn_decode_conv_step.  Against one fp64
+    oracle pass: o of every sequence and head at every step, and the whole
+    state at steps 1, 16 and 1000."""
     import torch
     inp = synth.decode_b64_bf16()
     sh = inp.shape
-    note(f"decode workload {inp.name}: B={inp.batch}")
-    B = inp.batch
+    B, steps = inp.batch, 1000
+    note(f"decode workload {inp.name}: B={B}, {steps} steps, both paths")
     x_dev = [to_dev(inp.x[p], "bf16") for p in range(inp.pool)]
     g_dev = [to_dev(inp.g[p]) for p in range(inp.pool)]
     b_dev = [to_dev(inp.beta[p]) for p in range(inp.pool)]
     w = to_dev(inp.conv_w)
-    cs = to_dev(inp.conv_state0, "bf16")
-    S = torch.from_numpy(inp.state0).cuda()
-    seqs = np.array([0, 17, 63])
     a = sh.num_qk_heads * sh.head_dim_k
-    checkpoints = {1: None, 16: None, 1000: None}
-    o_hist = []
-    for i in range(1000):
-        p = i % inp.pool
-        y = G.conv1d(x_dev[p], w, seqlen=1, num_seqs=B, conv_state=cs)
-        q = y[:, :a].view(B, sh.num_qk_heads, sh.head_dim_k)
-        k = y[:, a:2 * a].view(B, sh.num_qk_heads, sh.head_dim_k)
-        v = y[:, 2 * a:].view(B, sh.num_v_heads, sh.head_dim_v)
-        o = G.decode_step(q, k, v, g_dev[p], b_dev[p], S)
-        o_hist.append(o[torch.from_numpy(seqs).cuda()].float().cpu())
-        if i + 1 in checkpoints:
-            torch.cuda.synchronize()
-            checkpoints[i + 1] = S[torch.from_numpy(seqs).cuda()].cpu().numpy()
-    torch.cuda.synchronize()
-    note("  gpu done; running oracle on the sampled sequences")
-    outs, kept = _decode_pipeline_oracle(orc, inp, 1000, seqs, keep=(1, 16, 1000))
-    worst_o = 0.0
-    for i in range(1000):
-        worst_o = max(worst_o, rel_err_slices(o_hist[i].numpy(), outs[i], np.arange(len(seqs) + 1)))
-    note(f"  worst o err over 1000 steps: {worst_o:.2e}")
-    assert worst_o <= TOL["bf16"]
-    for n in (1, 16, 1000):
-        es = rel_err_slices(checkpoints[n], kept[n])
-        note(f"  S err at step {n}: {es:.2e}")
-        assert es <= TOL["bf16"]
+    keep = (1, 16, steps)
+    hist, kept = {}, {}
+    for path in ("two_calls", "fused"):
+        cs = to_dev(inp.conv_state0, "bf16")
+        S = torch.from_numpy(inp.state0).cuda()
+        o_all = torch.empty((steps, B, sh.num_v_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        fused = G.DecodeConv(x_dev[0], w, num_qk_heads=sh.num_qk_heads, num_v_heads=sh.num_v_heads,
+                             head_dim_k=sh.head_dim_k, head_dim_v=sh.head_dim_v, num_slots=B)
+        kept[path] = {}
+        for i in range(steps):
+            p = i % inp.pool
+            if path == "fused":
+                fused(x_dev[p], g_dev[p], b_dev[p], S, cs, o_all[i])
+            else:
+                y = G.conv1d(x_dev[p], w, seqlen=1, num_seqs=B, conv_state=cs)
+                q = y[:, :a].view(B, sh.num_qk_heads, sh.head_dim_k)
+                k = y[:, a:2 * a].view(B, sh.num_qk_heads, sh.head_dim_k)
+                v = y[:, 2 * a:].view(B, sh.num_v_heads, sh.head_dim_v)
+                G.decode_step(q, k, v, g_dev[p], b_dev[p], S, out=o_all[i])
+            if i + 1 in keep:
+                kept[path][i + 1] = S.cpu().numpy()
+        torch.cuda.synchronize()
+        hist[path] = o_all.view(torch.int16).cpu().numpy().view(np.uint16)  # bf16 bits, 0.5 GB
+        del o_all
+    note("  gpu done; running the oracle over every sequence")
+    ref = DecodePipelineOracle(orc, inp, np.arange(B))
+    cu = np.arange(B + 1)
+    worst = {path: 0.0 for path in hist}
+    for i in range(steps):
+        o_ref = ref.step()
+        for path in hist:
+            o_gpu = (hist[path][i].astype(np.uint32) << 16).view(np.float32)
+            worst[path] = max(worst[path], rel_err_slices(o_gpu, o_ref, cu))
+        if i + 1 in keep:
+            for path in hist:
+                es = rel_err_slices(kept[path][i + 1], ref.S)
+                note(f"  {path}: S err at step {i + 1}: {es:.2e}")
+                assert es <= TOL["bf16"], f"{path}: state at step {i + 1}"
+    for path in hist:
+        note(f"  {path}: worst o err over {steps} steps, all {B} sequences: {worst[path]:.2e}")
+        assert worst[path] <= TOL["bf16"], path
