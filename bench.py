@@ -8,13 +8,21 @@ the chunked prefill (phase 1 + phase 2) producing o and the final state.
 starts; 4 input/output buffer sets (~750 MB) are rotated so the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
+The roofline line is that of the chunked prefill itself, gdn_prefill_chunked
+(prepare + scan) timed as one call on the q/k/v column blocks of the conv
+output, against the layer's algorithmic bytes (HBM-bound) with its bf16
+matrix-core fraction beside it.  The adversarial fp32 (8192 tokens) and
+varlen bf16 (16 sequences) workloads get the same call timed on their own.
+
 The decode path (conv step + recurrent step, B=64, fp32 32x128x128 states,
-4 rotated state pools of 134 MB) is measured in the same run and reported
-under "decode", as two library calls and as the one fused call.  The timed loop runs the steps back to back with no event
-markers in it (a marker leaves the GPU idle for a few microseconds between
-calls).  Per-call times come from HIP events on the launch stream: each
-call alone, run back to back under one event pair (the per-launch time the
-roofline uses), and, separately, a marker after every call of a step.
+4 rotated state pools of 134 MB, 1000 steps) is measured in the same run and
+reported under "decode", as two library calls and as the one fused call.
+The timed loops run back to back with no event markers in them (a marker
+leaves the GPU idle for a few microseconds between calls).  Per-call times
+come from HIP events on the launch stream: each call alone, run back to
+back under one event pair (the per-launch time the roofline uses), in
+blocks of 10 launches for the spread (p10 / p50 / p90 of the block means),
+and, separately, a marker after every call of a step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -35,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # dense bf16 matrix
+FP32_PEAK_TFLOPS = 157.3       # fp32 matrix
 METRIC = "GDN prefill tokens/s per layer (T=4096) + decode step HBM GB/s, % roofline"
 
 
@@ -53,6 +62,23 @@ def prefill_alg_flops(T, hv, dk, dv, C=64):
     per_chunk = 2 * (C * (C - 1) / 2 * dk + C * (C + 1) / 2 * dk + C ** 3 / 6
                      + 2 * C * (C - 1) / 2 * dk + 3 * C * dk * dv + C * (C + 1) / 2 * dv)
     return per_chunk * (T / C) * hv
+
+
+def prefill_alg_flops_varlen(lens, hv, dk, dv, C=64):
+    """prefill_alg_flops summed over sequences chunked from their own starts,
+    a partial last chunk of C' tokens counted at C'."""
+    def chunk(c):
+        return 2 * (c * (c - 1) / 2 * dk + c * (c + 1) / 2 * dk + c ** 3 / 6
+                    + 2 * c * (c - 1) / 2 * dk + 3 * c * dk * dv + c * (c + 1) / 2 * dv)
+    return sum((int(n) // C * chunk(C) + (chunk(int(n) % C) if int(n) % C else 0)) * hv for n in lens)
+
+
+def percentiles(xs):
+    """mean, p10, p50, p90 of a list of per-launch times (us)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p50": round(float(np.percentile(a, 50)), 2), "p90": round(float(np.percentile(a, 90)), 2),
+            "blocks": int(a.size)}
 
 
 def conv_prepare_alg_bytes(T, C, hv, esize=2, W=4):
@@ -83,14 +109,17 @@ def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
 
 
 KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
+                  "prefill_chunked": ["prefill.hip", "prefill_seg.hip"],
                   "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip", "conv_math.h"],
                   "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"],
                   "gated_norm": ["gated_norm.hip"], "gating": ["gating.hip"]}
 # The GPU kernels each library call launches on the 4096-token bf16 layer
 # (conv_prepare: the convolution, then the chunk prepare; the scan call runs
-# the segment-parallel carry: two passes and a combine) and on the
+# the segment-parallel carry: two passes and a combine; prefill_chunked is
+# the prepare followed by the scan, the whole chunked prefill) and on the
 # 64-sequence decode step (two calls, or the one fused call).
 CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
+                "prefill_chunked": ["k_prepare", "k_seg_pass1", "k_seg_combine", "k_seg_pass2"],
                 "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
                 "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"],
                 "gated_norm": ["k_gated_norm"], "gating": ["k_gating"]}
@@ -144,7 +173,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--blocks", type=int, default=20, help="blocks of back-to-back launches for the percentiles")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the adversarial fp32 and varlen throughput lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=4, help="rotated buffer sets (MALL control)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -232,6 +264,22 @@ def main():
         torch.cuda.synchronize()
         return r0.elapsed_time(r1) * 1e3 / n
 
+    # The same in `blocks` blocks of `per` launches, one event pair per block:
+    # the mean per-launch time over all launches and the spread of the block
+    # means (p10 / p50 / p90).
+    def blocks_of(fn, per=10, blocks=None):
+        nb_ = blocks or args.blocks
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb_)]
+        torch.cuda.synchronize()
+        for b in range(nb_):
+            ev[b][0].record(stream)
+            for i in range(per):
+                fn(sets[(b * per + i) % nsets])
+            ev[b][1].record(stream)
+        torch.cuda.synchronize()
+        per_launch = [e0.elapsed_time(e1) * 1e3 / per for e0, e1 in ev]
+        return float(np.mean(per_launch)), percentiles(per_launch)
+
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
@@ -262,6 +310,21 @@ def main():
     nb = max(args.steps, 20)
     k_cp = back_to_back(lambda s: cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"]), nb)
     k_scan = back_to_back(lambda s: cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"]), nb)
+    # the whole chunked prefill as one library call (gdn_prefill_chunked:
+    # prepare + scan) on the q, k, v column blocks of each set's conv output
+    pc = gdn.Prefill(*cp.views(sets[0]["y"]), seqlen=T, chunk_size=64)
+
+    def prefill_call(s):
+        q_, k_, v_ = cp.views(s["y"])
+        pc(q_, k_, v_, s["g"], s["beta"], s["o"], None, s["st"])
+
+    for i in range(nsets):
+        prefill_call(sets[i])
+    k_pc = back_to_back(prefill_call, nb)
+    _, pct_pc = blocks_of(prefill_call)
+    _, pct_cp = blocks_of(lambda s: cp.conv_prepare(s["x"], s["y"], s["g"], s["beta"]))
+    _, pct_scan = blocks_of(lambda s: cp.scan(s["y"], s["g"], s["beta"], s["o"], None, s["st"]))
+    _, pct_step = blocks_of(step)
     norm = gdn.GatedNorm(sets[0]["o"], sets[0]["z"], wn, y=sets[0]["yn"])
     for i in range(nsets):  # its first launches, before the timed run
         norm(sets[i]["o"], sets[i]["z"], sets[i]["yn"])
@@ -310,15 +373,20 @@ def main():
     F_pre = prefill_alg_flops(T, sh.num_v_heads, sh.head_dim_k, sh.head_dim_v)
     B_cp = conv_prepare_alg_bytes(T, CC, sh.num_v_heads)
     kernels = {"conv_prepare": float(k_cp), "prefill_scan": float(k_scan)}
-    dominant = max(kernels, key=kernels.get)
-    dom_us = kernels[dominant]
-    dom_bytes = {"conv_prepare": B_cp, "prefill_scan": B_pre}[dominant]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = read_traffic(dominant, inp.name)
-    roofline = {"bound": "hbm", "kernel": dominant, "gpu_kernels": CALL_KERNELS[dominant],
+    # The roofline is that of the chunked prefill, gdn_prefill_chunked timed
+    # as one call: the layer's algorithmic bytes (q, k, v, o, g, beta and the
+    # final state) and flops over its per-launch time.  Arithmetic intensity
+    # 177 flop/B is below the chip's ridge (2516.6 TFLOP/s / 8 TB/s = 315), so
+    # HBM bounds it; the bf16 matrix-core fraction is given beside.
+    achieved = B_pre / (k_pc * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "prefill_chunked", "gpu_kernels": CALL_KERNELS["prefill_chunked"],
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "alg_bytes_per_launch": int(dom_bytes),
-                "avg_launch_us": round(dom_us, 2)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("prefill_chunked", inp.name),
+                "alg_bytes_per_launch": int(B_pre), "alg_flops_per_launch": int(F_pre),
+                "avg_launch_us": round(k_pc, 2), "launch_us_blocks": pct_pc,
+                "tokens_per_s": round(T / (k_pc * 1e-6), 1),
+                "mfma_bf16": {"achieved": round(F_pre / (k_pc * 1e-6) / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(F_pre / (k_pc * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
     step_us = kernels["conv_prepare"] + kernels["prefill_scan"]
 
     # ----------------------------------------------------------------- decode
@@ -381,6 +449,19 @@ def main():
     r1.record(stream)
     torch.cuda.synchronize()
     d_step = r0.elapsed_time(r1) * 1e3 / nrun
+
+    def decode_blocks(fn, per=10):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.blocks)]
+        torch.cuda.synchronize()
+        for b in range(args.blocks):
+            ev[b][0].record(stream)
+            for i in range(per):
+                fn(b * per + i)
+            ev[b][1].record(stream)
+        torch.cuda.synchronize()
+        return percentiles([e0.elapsed_time(e1) * 1e3 / per for e0, e1 in ev])
+
+    pct_dec = decode_blocks(lambda i: dec(qd, kd, vd, gs[i % dinp.pool], bs[i % dinp.pool], pools[i % npool], od))
     B_dec = decode_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v)
     dec_gbs = B_dec / (d_step * 1e-6) / 1e9
 
@@ -408,6 +489,7 @@ def main():
     r1.record(stream)
     torch.cuda.synchronize()
     f_step = r0.elapsed_time(r1) * 1e3 / nrun
+    pct_fused = decode_blocks(fstep)
     B_fused = decode_conv_alg_bytes(Bd, dsh.num_qk_heads, dsh.num_v_heads, dsh.head_dim_k, dsh.head_dim_v,
                                     W=dinp.conv_w.shape[1])
     fused_gbs = B_fused / (f_step * 1e-6) / 1e9
@@ -420,7 +502,7 @@ def main():
                            "achieved": round(dec_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                            "traffic": read_traffic("decode_step", dinp.name), "alg_bytes_per_launch": int(B_dec),
-                           "avg_launch_us": round(d_step, 2)},
+                           "avg_launch_us": round(d_step, 2), "launch_us_blocks": pct_dec},
               "fused_conv_step": {
                   "decode_conv_step_us": round(f_step, 2),
                   "ms_per_token_step_wall": round(fwall * 1e3 / args.decode_steps, 4),
@@ -429,7 +511,8 @@ def main():
                                "gpu_kernels": CALL_KERNELS["decode_conv_step"], "achieved": round(fused_gbs, 1),
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                                "traffic": read_traffic("decode_conv_step", dinp.name),
-                               "alg_bytes_per_launch": int(B_fused), "avg_launch_us": round(f_step, 2)}}}
+                               "alg_bytes_per_launch": int(B_fused), "avg_launch_us": round(f_step, 2),
+                               "launch_us_blocks": pct_fused}}}
 
     # ------------------------------------- multi-layer decode, eager vs graph
     # A token's step through `layers` layers of the fused, gated decode step
@@ -495,6 +578,67 @@ def main():
 
     decode["multilayer_graph"] = [decode_graph_figures(1), decode_graph_figures(Bd)]
 
+    # ------------------------------- the adversarial and varlen prefill lines
+    # gdn_prefill_chunked alone on the other two prefill workloads: 8192
+    # tokens of repeated keys in fp32 (one sequence), and 16 packed bf16
+    # sequences with initial states.  Their inputs (268 MB and 981 MB of
+    # conv output) exceed the 256 MB Infinity Cache, so no rotation is needed.
+    extra = None
+    if not args.no_extra_workloads:
+        extra = {}
+        for key, make in (("adversarial_fp32", synth.adversarial_8k_fp32), ("varlen_bf16", synth.varlen_bf16)):
+            winp = make()
+            wsh = winp.shape
+            tdt = torch.bfloat16 if winp.dtype == "bf16" else torch.float32
+            esz = 2 if winp.dtype == "bf16" else 4
+            Tw = winp.total_tokens
+            xw = torch.from_numpy(winp.x).to(tdt).to(dev)
+            cuw = None if winp.dense_T else torch.from_numpy(winp.cu_seqlens).to(dev)
+            yw = gdn.conv1d(xw, torch.from_numpy(winp.conv_w).to(dev), cu_seqlens=cuw,
+                            seqlen=winp.dense_T or None, num_seqs=winp.num_seqs)
+            del xw
+            aw = wsh.num_qk_heads * wsh.head_dim_k
+            qw = yw[:, :aw].view(Tw, wsh.num_qk_heads, wsh.head_dim_k)
+            kw = yw[:, aw:2 * aw].view(Tw, wsh.num_qk_heads, wsh.head_dim_k)
+            vw = yw[:, 2 * aw:].view(Tw, wsh.num_v_heads, wsh.head_dim_v)
+            gw, bw = torch.from_numpy(winp.g).to(dev), torch.from_numpy(winp.beta).to(dev)
+            s0w = None if winp.state0 is None else torch.from_numpy(winp.state0).to(dev)
+            ow = torch.empty((Tw, wsh.num_v_heads, wsh.head_dim_v), dtype=tdt, device=dev)
+            stw = torch.empty((winp.num_seqs, wsh.num_v_heads, wsh.head_dim_k, wsh.head_dim_v), dtype=torch.float32,
+                              device=dev)
+            pw = gdn.Prefill(qw, kw, vw, cu_seqlens=cuw, seqlen=winp.dense_T or None, num_seqs=winp.num_seqs,
+                             chunk_size=64)
+            for _ in range(3):
+                pw(qw, kw, vw, gw, bw, ow, s0w, stw)
+            nw = 20
+            r0.record(stream)
+            for _ in range(nw):
+                pw(qw, kw, vw, gw, bw, ow, s0w, stw)
+            r1.record(stream)
+            torch.cuda.synchronize()
+            t_w = r0.elapsed_time(r1) * 1e3 / nw
+            lens = np.diff(winp.cu_seqlens)
+            Bw = prefill_alg_bytes(Tw, wsh.num_qk_heads, wsh.num_v_heads, wsh.head_dim_k, wsh.head_dim_v,
+                                   n_seq=winp.num_seqs, esize=esz, state_in=s0w is not None)
+            Fw = prefill_alg_flops_varlen(lens, wsh.num_v_heads, wsh.head_dim_k, wsh.head_dim_v)
+            hbm = Bw / (t_w * 1e-6) / 1e9
+            if winp.dtype == "f32":   # fp32 operands: the fp32 matrix rate bounds it (36.8 GFLOP vs 407 MB)
+                rl = {"bound": "mfma", "achieved": round(Fw / (t_w * 1e-6) / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(Fw / (t_w * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                      "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
+            else:
+                rl = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(hbm / HBM_PEAK_GBS, 4),
+                      "mfma_bf16_frac": round(Fw / (t_w * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            rl.update({"kernel": "prefill_chunked", "traffic": read_traffic("prefill_chunked", winp.name),
+                       "alg_bytes_per_launch": int(Bw), "alg_flops_per_launch": int(Fw),
+                       "avg_launch_us": round(t_w, 2)})
+            extra[key] = {"workload": winp.name, "tokens": Tw, "sequences": winp.num_seqs, "dtype": winp.dtype,
+                          "prefill_chunked_us": round(t_w, 2), "tokens_per_s": round(Tw / (t_w * 1e-6), 1),
+                          "roofline": rl}
+            del yw, qw, kw, vw, ow, stw, pw, s0w, gw, bw
+            torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -509,9 +653,20 @@ def main():
                                    return_threads=True)
             reps += 1
         ct = time.perf_counter() - t0
+        # and on one core: the whole workload once (the conv is single-threaded
+        # in both figures)
+        t1 = time.perf_counter()
+        y64, _ = oracle.conv1d(inp.x, inp.conv_w)
+        qo, ko, vo = synth.split_qkv(y64, sh)
+        oracle.scan(qo, ko, vo, inp.g, inp.beta, n_threads=1)
+        c1 = time.perf_counter() - t1
         cpu = {"value": round(reps * T / ct, 1), "unit": "tokens/s", "cores": int(nt), "kind": "oracle",
                "sample": f"the whole workload {reps} times: fp64 conv1d+SiLU over {T}x{CC} and the token-by-token "
-                         f"scan of all {sh.num_v_heads} v-heads x {T} tokens, {ct:.2f} s on {cpu_model()}"}
+                         f"scan of all {sh.num_v_heads} v-heads x {T} tokens, {ct:.2f} s on {cpu_model()} "
+                         f"({oracle.available_cores()} cores in the affinity mask; the scan is threaded over "
+                         f"(sequence, v-head) on at most 16, the box's CPU share for one GPU)",
+               "one_core": {"value": round(T / c1, 1), "unit": "tokens/s", "cores": 1,
+                            "sample": f"the whole workload once on one thread, {c1:.2f} s"}}
 
     out = {
         "metric": METRIC,
@@ -533,8 +688,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v, 2) for k, v in kernels.items()},
+        "kernels_us_blocks": {"conv_prepare": pct_cp, "prefill_scan": pct_scan, "step": pct_step},
         "kernels_us_per_call_events": {"conv_prepare": round(k_cp_ev, 2), "prefill_scan": round(k_scan_ev, 2)},
         "gpu_ms_per_step_events": round(gpu_ms / args.steps, 5),
+        "prefill_chunked_us": round(k_pc, 2),
         "step_kernels": {"us": round(step_us, 2), "tokens_per_s": round(T / (step_us * 1e-6), 1),
                          "hbm_frac": round(B_pre / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "mfma_frac_bf16": round(F_pre / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -543,6 +700,7 @@ def main():
         "gated_norm": gated_norm,
         "gating": gating,
         "decode": decode,
+        "prefill_workloads": extra,
         "source_digest": {k: source_digest(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(out), flush=True)

@@ -70,3 +70,21 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_varlen_flops_match_dense_on_whole_chunks():
+    # whole chunks: the same as the dense count; a partial chunk counts at its length
+    assert bench.prefill_alg_flops_varlen([4096], 32, 128, 128) == pytest.approx(
+        bench.prefill_alg_flops(4096, 32, 128, 128))
+    assert bench.prefill_alg_flops_varlen([64, 128], 2, 128, 128) == pytest.approx(
+        bench.prefill_alg_flops(192, 2, 128, 128))
+    tail = bench.prefill_alg_flops_varlen([70], 1, 128, 128) - bench.prefill_alg_flops(64, 1, 128, 128)
+    # 6 tokens: 2 (6*5/2*128 + 6*7/2*128 + 6^3/6 + 2*6*5/2*128 + 3*6*128*128 + 6*7/2*128)
+    assert tail == pytest.approx(2 * (15 * 128 + 21 * 128 + 36 + 30 * 128 + 3 * 6 * 128 * 128 + 21 * 128))
+    assert bench.prefill_alg_flops_varlen([0, 0], 4, 64, 64) == 0
+
+
+def test_percentiles():
+    p = bench.percentiles([1.0, 2.0, 3.0, 4.0, 5.0])
+    assert p["mean"] == 3.0 and p["p50"] == 3.0 and p["blocks"] == 5
+    assert p["p10"] == pytest.approx(1.4) and p["p90"] == pytest.approx(4.6)
