@@ -426,6 +426,52 @@ gdn_status gdn_decode_conv_gated_step(const gdn_dims *d,
                                       const int32_t *state_slots, void *o,
                                       void *stream);
 
+/*
+ * Recurrent-state snapshots for prefix caching.  The per-sequence state --
+ * the fp32 memories of all v-heads and the causal-conv window -- lives in a
+ * caller-owned slot per (sequence, layer); a prompt prefix is reused by
+ * restoring the state saved at its end rather than recomputing it
+ * (Vallmo.jl README, "What's here": recurrent state snapshot/restore gives
+ * prefix caching; PicoLM fork changelog, "SSM State Checkpointing": the state
+ * is saved periodically during prefill and generation, and the nearest
+ * saved state is restored on partial reuse).  One layer per call.
+ *
+ * gdn_snapshot_push copies, for each of num_seqs sequences b, live slot
+ * slots[b] (or b when slots is NULL) of
+ *     state      fp32 [num_slots][state_elems]   (state_elems = H_v d_k d_v)
+ *     conv_state      [num_slots][window_bytes]  ((W-1) C_conv elements)
+ * into entry e = (*ring_head mod ring_len) of the caller's ring
+ *     ring_state  fp32 [ring_len][num_seqs][state_elems]
+ *     ring_window      [ring_len][num_seqs][window_bytes]
+ * and then adds one to *ring_head (a device int32 counting the pushes; the
+ * caller sets it, normally to 0).  The entry is read on the device, so a
+ * captured decode graph can push every N tokens with no host work; entry
+ * n mod ring_len then holds push number n (the caller keeps the count on
+ * the host, or reads the counter back).  Pushes sharing a counter must be
+ * ordered (one stream).
+ *
+ * gdn_snapshot_restore copies ring entry `entry` (host int in [0, ring_len))
+ * back into the live slots slots[b] (or b), state and window.  Continuing
+ * from a restored entry gives, bit for bit, what continuing from the pushed
+ * moment gave: the copies are exact.
+ *
+ * state_elems: a multiple of 4 (>= 0); window_bytes: a multiple of 16
+ * (>= 0; 0 with conv_state and ring_window NULL copies states only).  All
+ * pointers 16-byte aligned (slots and ring_head 4), device memory; the live
+ * slots and the ring must not overlap.  A slot index outside [0, num_slots)
+ * skips that sequence (its ring entry and slot are left as they were).
+ * Errors as the other calls; nothing is queued on an invalid argument.
+ */
+gdn_status gdn_snapshot_push(int32_t num_seqs, const int32_t *slots, int32_t num_slots,
+                             int64_t state_elems, const float *state, int64_t window_bytes,
+                             const void *conv_state, int32_t ring_len, float *ring_state,
+                             void *ring_window, int32_t *ring_head, void *stream);
+
+gdn_status gdn_snapshot_restore(int32_t num_seqs, const int32_t *slots, int32_t num_slots,
+                                int64_t state_elems, float *state, int64_t window_bytes,
+                                void *conv_state, int32_t ring_len, const float *ring_state,
+                                const void *ring_window, int32_t entry, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "conv1d.hip", "decode.hip", "prefill.hip", "prefill_seg.hip", "gated_norm.hip", "gating.hip", "debug.hip"]
+SOURCES = ["gdn_api.cpp", "conv1d.hip", "decode.hip", "prefill.hip", "prefill_seg.hip", "gated_norm.hip", "gating.hip", "snapshot.hip", "debug.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

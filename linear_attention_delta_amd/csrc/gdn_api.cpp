@@ -808,6 +808,76 @@ gdn_status gdn_gating(int32_t total_tokens, int32_t num_heads, int32_t dtype, co
   return ok();
 }
 
+static gdn_status snapshot_impl(int32_t num_seqs, const int32_t* slots, int32_t num_slots, int64_t state_elems,
+                                const void* state, int64_t window_bytes, const void* conv_state, int32_t ring_len,
+                                const void* ring_state, const void* ring_window, int32_t* ring_head, int32_t entry,
+                                int to_ring, void* stream) {
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_slots < 1) return fail(GDN_ERR_INVALID_ARG, "num_slots must be >= 1");
+  if (!slots && num_slots < num_seqs)
+    return fail(GDN_ERR_INVALID_ARG, "without slots, num_slots (%d) must be >= num_seqs (%d)", num_slots, num_seqs);
+  if (slots && !aligned(slots, 4)) return fail(GDN_ERR_INVALID_ARG, "slots must be 4-byte aligned");
+  if (ring_len < 1) return fail(GDN_ERR_INVALID_ARG, "ring_len must be >= 1");
+  if (state_elems < 0 || state_elems % 4 || window_bytes < 0 || window_bytes % 16)
+    return fail(GDN_ERR_INVALID_ARG, "state_elems must be a multiple of 4 and window_bytes of 16 (both >= 0)");
+  if (state_elems > (1LL << 36) || window_bytes > (1LL << 38))
+    return fail(GDN_ERR_UNSUPPORTED, "per-slot sizes above 2^36 elements / 2^38 bytes are not supported");
+  if (state_elems > 0 && (!state || !ring_state || !aligned(state, 16) || !aligned(ring_state, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "state and ring_state must be non-NULL and 16-byte aligned");
+  if (window_bytes > 0 && (!conv_state || !ring_window || !aligned(conv_state, 16) || !aligned(ring_window, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "conv_state and ring_window must be non-NULL and 16-byte aligned");
+  if (to_ring) {
+    if (!ring_head || !aligned(ring_head, 4)) return fail(GDN_ERR_INVALID_ARG, "ring_head must be non-NULL and 4-byte aligned");
+  } else if (entry < 0 || entry >= ring_len) {
+    return fail(GDN_ERR_INVALID_ARG, "entry (%d) must be in [0, ring_len = %d)", entry, ring_len);
+  }
+  auto overlap = [](const void* p, size_t pn, const void* q, size_t qn) {
+    const char* x = reinterpret_cast<const char*>(p);
+    const char* y = reinterpret_cast<const char*>(q);
+    return pn && qn && x < y + qn && y < x + pn;
+  };
+  const size_t sb = (size_t)state_elems * 4, wb = (size_t)window_bytes;
+  const size_t live_s = (size_t)num_slots * sb, live_w = (size_t)num_slots * wb;
+  const size_t ring_s = (size_t)ring_len * num_seqs * sb, ring_w = (size_t)ring_len * num_seqs * wb;
+  if (overlap(state, live_s, ring_state, ring_s) || overlap(conv_state, live_w, ring_window, ring_w) ||
+      overlap(state, live_s, ring_window, ring_w) || overlap(conv_state, live_w, ring_state, ring_s))
+    return fail(GDN_ERR_INVALID_ARG, "the live slots and the ring must not overlap");
+  if (num_seqs == 0 || (sb == 0 && wb == 0)) {
+    if (!to_ring) return ok();
+  }
+  gdn::SnapArgs a;
+  a.num_seqs = num_seqs;
+  a.num_slots = num_slots;
+  a.ring_len = ring_len;
+  a.entry = entry;
+  a.slots = slots;
+  a.state_bytes = (long)sb;
+  a.window_bytes = (long)wb;
+  a.state = const_cast<void*>(state);
+  a.window = const_cast<void*>(conv_state);
+  a.ring_state = const_cast<void*>(ring_state);
+  a.ring_window = const_cast<void*>(ring_window);
+  a.head = to_ring ? ring_head : nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_snapshot(a, to_ring, s);
+  if (e != hipSuccess) return hip_fail(e, to_ring ? "snapshot push launch" : "snapshot restore launch");
+  return ok();
+}
+
+gdn_status gdn_snapshot_push(int32_t num_seqs, const int32_t* slots, int32_t num_slots, int64_t state_elems,
+                             const float* state, int64_t window_bytes, const void* conv_state, int32_t ring_len,
+                             float* ring_state, void* ring_window, int32_t* ring_head, void* stream) {
+  return snapshot_impl(num_seqs, slots, num_slots, state_elems, state, window_bytes, conv_state, ring_len, ring_state,
+                       ring_window, ring_head, 0, 1, stream);
+}
+
+gdn_status gdn_snapshot_restore(int32_t num_seqs, const int32_t* slots, int32_t num_slots, int64_t state_elems,
+                                float* state, int64_t window_bytes, void* conv_state, int32_t ring_len,
+                                const float* ring_state, const void* ring_window, int32_t entry, void* stream) {
+  return snapshot_impl(num_seqs, slots, num_slots, state_elems, state, window_bytes, conv_state, ring_len, ring_state,
+                       ring_window, nullptr, entry, 0, stream);
+}
+
 gdn_status gdn_validate(const gdn_dims* d, int32_t op, const void* const* ptrs, int32_t n_ptrs, int64_t extent) {
   if (op != 0 && op != 1) return fail(GDN_ERR_INVALID_ARG, "op must be 0 (prefill) or 1 (decode)");
   const int32_t need = op == 0 ? 10 : 8;

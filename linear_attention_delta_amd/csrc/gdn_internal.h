@@ -70,6 +70,13 @@ struct ScanArgs {
   long stride_ga, stride_gb;
   const float* A_log;
   const float* dt_bias;
+  // the gated RMS norm fused into the carry's output write, where norm_z is
+  // set: o then receives y = w * o / sqrt(mean(o^2) + eps) * silu(z) per
+  // (token, v-head) row, z [N_tok][H_v][d_v] with token stride stride_z
+  const void* norm_z;
+  long stride_z;
+  const float* norm_w;
+  float norm_eps;
 };
 
 // Gated RMS norm over rows of d_v values (one row per token and v-head;
@@ -98,7 +105,24 @@ struct GatingArgs {
   float* beta;
 };
 
+// A push or restore of state snapshots: per sequence b, live slot slots[b]
+// (or b) of state [num_slots][state_bytes] and window [num_slots][window_bytes]
+// against ring entry e of ring_state [ring_len][num_seqs][state_bytes] and
+// ring_window [ring_len][num_seqs][window_bytes]; e = *head mod ring_len
+// (push, then the counter is advanced) or `entry`.
+struct SnapArgs {
+  int num_seqs, num_slots, ring_len, entry;
+  const int32_t* slots;
+  long state_bytes, window_bytes;  // multiples of 16
+  void* state;
+  void* window;
+  void* ring_state;
+  void* ring_window;
+  int* head;
+};
+
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
+hipError_t launch_snapshot(const SnapArgs& a, int to_ring, hipStream_t s);
 hipError_t launch_gated_norm(const NormArgs& a, hipStream_t s);
 hipError_t launch_gating(const GatingArgs& a, hipStream_t s);
 hipError_t launch_chunk_table(const ScanArgs& a, hipStream_t s);

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_validate", "gdn_conv1d",
             "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
             "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
-            "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step"]
+            "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step",
+            "gdn_snapshot_push", "gdn_snapshot_restore"]
 
 
 class GdnDims(ctypes.Structure):
@@ -80,6 +81,8 @@ def _load():
         "gdn_gating": ([i32, i32, i32, P, i64, P, i64, P, P, P, P, P], i32),
         "gdn_prefill_conv_gated": ([D, GI, i32, P, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gdn_decode_conv_gated_step": ([D, GI, i32, P, i64, P, P, P, P, i32, P, P, P], i32),
+        "gdn_snapshot_push": ([i32, P, i32, i64, P, i64, P, i32, P, P, P, P], i32),
+        "gdn_snapshot_restore": ([i32, P, i32, i64, P, i64, P, i32, P, P, i32, P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -536,3 +539,33 @@ def decode_conv_gated_step(step: "DecodeConv", x, gates: GdnGateInputs, state, c
                                           *step._w, conv_state.data_ptr(), state.data_ptr(), step.num_slots,
                                           _ptr(state_slots), out.data_ptr(), step._stream))
     return out
+
+
+class SnapshotRing:
+    """A device ring of `ring_len` snapshots of the live state (and conv
+    window) slots of one layer, for num_seqs sequences: push() copies the
+    slots into entry (*head mod ring_len) and advances the device counter
+    `head`; restore(e) copies entry e back.  Memory is torch's; the copies
+    are the library's kernels."""
+
+    def __init__(self, state, conv_state, num_seqs, ring_len, *, slots=None):
+        import torch
+        self.num_slots = state.shape[0]
+        self.state_elems = state[0].numel()
+        self.window_bytes = 0 if conv_state is None else conv_state[0].numel() * conv_state.element_size()
+        self.num_seqs, self.ring_len, self.slots = int(num_seqs), int(ring_len), slots
+        dev = state.device
+        self.ring_state = torch.empty((ring_len, num_seqs) + tuple(state.shape[1:]), dtype=torch.float32, device=dev)
+        self.ring_window = None if conv_state is None else torch.empty(
+            (ring_len, num_seqs) + tuple(conv_state.shape[1:]), dtype=conv_state.dtype, device=dev)
+        self.head = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def push(self, state, conv_state, stream=None):
+        _check(lib.gdn_snapshot_push(self.num_seqs, _ptr(self.slots), self.num_slots, self.state_elems, _ptr(state),
+                                     self.window_bytes, _ptr(conv_state), self.ring_len, _ptr(self.ring_state),
+                                     _ptr(self.ring_window), _ptr(self.head), _stream(stream)))
+
+    def restore(self, entry, state, conv_state, stream=None):
+        _check(lib.gdn_snapshot_restore(self.num_seqs, _ptr(self.slots), self.num_slots, self.state_elems,
+                                        _ptr(state), self.window_bytes, _ptr(conv_state), self.ring_len,
+                                        _ptr(self.ring_state), _ptr(self.ring_window), int(entry), _stream(stream)))

@@ -335,3 +335,32 @@ def test_validate_whole_calls(g):
     assert g.validate(dd, g.OP_DECODE, p, 8) == 1                    # misaligned slot array
     assert g.validate(dd, g.OP_DECODE, dgood[:7], 64) == 1
     assert g.validate(dd, 2, dgood, 64) == 1
+
+
+def test_snapshot_calls_reject_before_any_gpu_call(g):
+    L = g.lib
+    se, wb = 32 * 128 * 128, 3 * 8192 * 2
+    ok_args = dict(n=4, slots=None, nslots=4, se=se, st=1 << 30, wb=wb, win=2 << 30, ring=3, rs=3 << 30, rw=4 << 30)
+
+    def push(**kw):
+        a = dict(ok_args, **kw)
+        return L.gdn_snapshot_push(a["n"], a["slots"], a["nslots"], a["se"], a["st"], a["wb"], a["win"], a["ring"],
+                                   a["rs"], a["rw"], kw.get("head", 5 << 30), None)
+
+    def restore(entry, **kw):
+        a = dict(ok_args, **kw)
+        return L.gdn_snapshot_restore(a["n"], a["slots"], a["nslots"], a["se"], a["st"], a["wb"], a["win"],
+                                      a["ring"], a["rs"], a["rw"], entry, None)
+
+    assert push(nslots=3) == 1                      # fewer slots than sequences, no slot list
+    assert push(slots=18) == 1                      # misaligned slot list
+    assert push(ring=0) == 1
+    assert push(se=se + 2) == 1 and push(wb=wb + 8) == 1
+    assert push(st=None) == 1 and push(st=(1 << 30) + 8) == 1
+    assert push(win=None) == 1 and push(rw=(4 << 30) + 4) == 1
+    assert push(head=None) == 1 and push(head=(5 << 30) + 2) == 1
+    assert push(rs=(1 << 30) + 4 * se) == 1         # ring overlaps the live states
+    assert restore(3) == 1 and restore(-1) == 1    # entry outside the ring
+    # valid calls get as far as the launch (no GPU here)
+    assert push() == 4 and restore(2) == 4
+    assert push(wb=0, win=None, rw=None) == 4      # states only
