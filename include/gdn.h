@@ -214,6 +214,26 @@ gdn_status gdn_prefill_chunked(const gdn_dims *d, const void *q, const void *k,
                                size_t ws_bytes, void *stream);
 
 /*
+ * gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is instead a 64 MiB
+ * device array inside the library (one per GPU, held until the process
+ * ends; it fits the 4096-token layer with 16 q/k and 32 v-heads of 128 in
+ * bf16, which needs 62.9 MB).  Problems whose gdn_prefill_workspace_size
+ * exceeds 64 MiB return GDN_ERR_UNSUPPORTED before any HIP call.  Allocates
+ * nothing and frees nothing.  Every call on one GPU shares that GPU's array
+ * (each call writes every workspace byte it reads, so no clearing is
+ * needed): calls that overlap in time on one GPU -- on different streams,
+ * or from different host threads -- race and must not be issued.  The
+ * first call on a device looks the array's address up (a HIP runtime
+ * query, no allocation).  Arguments and results as gdn_prefill_chunked.
+ */
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims *d, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta,
+                                       const float *state_in, const int32_t *cu_seqlens,
+                                       void *o, float *state_out, void *stream);
+
+/*
  * Phase 1 of the prefill: everything that does not depend on the carried
  * state (the oxydllm notes, "Performance": the cross-chunk loop precomputes
  * all state-independent work in batch).  For every chunk and v-head it

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gdn.h"
@@ -295,6 +296,35 @@ gdn_status run_scan(gdn::ScanArgs& a, const gdn_dims* d, hipStream_t s) {
                      GDN_F32);
 }
 
+// ---- The no-allocation prefill's workspace: a file-scope device array.
+// Each GPU the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel or a copy: the name
+// is a host-side stand-in, not a device address.  The address comes from
+// hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+gdn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device index %d is not below %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(GDN_ERR_HIP, "scratch array address is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,6 +481,26 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* q, const void* k, 
   if (st != GDN_OK) return st;
   if ((st = gdn_prefill_prepare(d, q, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
   return gdn_prefill_scan(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta, const float* state_in,
+                                       const int32_t* cu_seqlens, void* o, float* state_out, void* stream) {
+  gdn_status st = check_dims(d, 0);
+  if (st != GDN_OK) return st;
+  const size_t need = ws_layout(d).total;
+  if (need > kScratchBytes)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "this problem needs %zu bytes of workspace, more than the %zu the no-allocation prefill holds; "
+                "call gdn_prefill_chunked with a workspace instead", need, kScratchBytes);
+  // every argument check first (a stand-in workspace address: the real one
+  // is known only after a HIP call), so an invalid call makes none
+  if ((st = validate_prefill(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out,
+                             reinterpret_cast<void*>(uintptr_t(256)), kScratchBytes)) != GDN_OK)
+    return st;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != GDN_OK) return st;
+  return gdn_prefill_chunked(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, ws, kScratchBytes, stream);
 }
 
 static gdn_status conv_prepare_impl(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,

@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_HIP", 5: "GDN_ERR_NONFINITE"}
 
 EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_dims", "gdn_validate", "gdn_conv1d",
-            "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
+            "gdn_prefill_workspace_size", "gdn_prefill_chunked", "gdn_prefill_chunked_noalloc", "gdn_prefill_prepare",
+            "gdn_prefill_scan",
             "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
             "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step",
             "gdn_snapshot_push", "gdn_snapshot_restore"]
@@ -71,6 +72,7 @@ def _load():
         "gdn_conv1d": ([i32, i32, i32, P, i32, i32, i32, P, i64, P, P, P, i32, P, i64, P], i32),
         "gdn_prefill_workspace_size": ([D], sz),
         "gdn_prefill_chunked": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
+        "gdn_prefill_chunked_noalloc": ([D, P, P, P, P, P, P, P, P, P, P], i32),
         "gdn_prefill_prepare": ([D, P, P, P, P, P, P, sz, P], i32),
         "gdn_prefill_scan": ([D, P, P, P, P, P, P, P, P, P, P, sz, P], i32),
         "gdn_prefill_conv_prepare": ([D, i32, P, i64, P, P, P, P, P, P, P, i64, P, sz, P], i32),
@@ -283,6 +285,25 @@ def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, nu
     p(q, k, v, g, beta, out, state_in, state_out, stream)
     _keep_for_stream(stream, p.ws, out, state_out)
     return out, state_out
+
+
+def prefill_noalloc(q, k, v, g, beta, o, state_out, *, state_in=None, cu_seqlens=None, seqlen=None,
+                    num_seqs=None, chunk_size=64, l2norm=True, heads_tiled=False, scale=1.0, stream=None):
+    """gdn_prefill_chunked_noalloc: the chunked prefill with the library's own
+    device workspace (no workspace argument).  o and state_out are the
+    caller's; nothing is allocated here or in the library."""
+    n_tok = q.shape[0]
+    if cu_seqlens is not None:
+        num_seqs, seqlen = cu_seqlens.numel() - 1, 0
+    else:
+        seqlen = int(seqlen if seqlen is not None else n_tok)
+        num_seqs = int(num_seqs if num_seqs is not None else (n_tok // seqlen if seqlen else 1))
+    d = _dims_for(q, k, v, num_seqs=num_seqs, seqlen=seqlen, chunk_size=chunk_size, l2norm=l2norm,
+                  heads_tiled=heads_tiled, scale=scale)
+    _check(lib.gdn_prefill_chunked_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(state_in), _ptr(cu_seqlens), _ptr(o), _ptr(state_out),
+                                           _stream(stream)))
+    return o, state_out
 
 
 class ConvPrefill:
