@@ -109,6 +109,7 @@ def decode_conv_alg_bytes(B, hk, hv, dk, dv, W=4, esize=2):
 
 
 KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
+                  "scan_gated_norm": ["prefill.hip", "prefill_seg.hip"],
                   "prefill_chunked": ["prefill.hip", "prefill_seg.hip"],
                   "prefill_scan": ["prefill.hip", "prefill_seg.hip"], "decode_step": ["decode.hip", "conv_math.h"],
                   "conv_step": ["conv1d.hip", "conv_math.h"], "decode_conv_step": ["decode.hip", "conv_math.h"],
@@ -120,7 +121,8 @@ KERNEL_SOURCES = {"conv_prepare": ["conv1d.hip", "conv_math.h", "prefill.hip"],
 # 64-sequence decode step (two calls, or the one fused call).
 CALL_KERNELS = {"conv_prepare": ["k_conv1d", "k_prepare"],
                 "prefill_chunked": ["k_prepare", "k_seg_pass1", "k_seg_combine", "k_seg_pass2"],
-                "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
+                "prefill_scan": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"],
+                "scan_gated_norm": ["k_seg_pass1", "k_seg_combine", "k_seg_pass2"], "decode_step": ["k_decode"],
                 "conv_step": ["k_conv_step"], "decode_conv_step": ["k_decode_conv"],
                 "gated_norm": ["k_gated_norm"], "gating": ["k_gating"]}
 
@@ -349,7 +351,15 @@ def main():
                            "frac": round(B_gate / (k_gate * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": read_traffic("gating", inp.name), "alg_bytes_per_launch": int(B_gate),
                            "avg_launch_us": round(k_gate, 2)}}
+    # the carry with the norm fused into its output write (o never goes
+    # through memory), against the carry followed by the norm
+    for i in range(nsets):
+        cp.scan_gated_norm(sets[i]["y"], sets[i]["g"], sets[i]["beta"], sets[i]["z"], wn, sets[i]["yn"], None,
+                           sets[i]["st"])
+    k_scan_norm = back_to_back(lambda s: cp.scan_gated_norm(s["y"], s["g"], s["beta"], s["z"], wn, s["yn"], None,
+                                                            s["st"]), nb)
     gated_norm = {"gated_norm_us": round(k_norm, 2),
+                  "scan_gated_norm_us": round(k_scan_norm, 2), "scan_then_gated_norm_us": round(k_scan + k_norm, 2),
                   "roofline": {"bound": "hbm", "kernel": "gated_norm", "gpu_kernels": CALL_KERNELS["gated_norm"],
                                "achieved": round(B_norm / (k_norm * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": round(B_norm / (k_norm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -261,6 +261,45 @@ gdn_status gdn_prefill_scan(const gdn_dims *d, const void *q, const void *k,
                             size_t ws_bytes, void *stream);
 
 /*
+ * The prefill's carry (gdn_prefill_scan) with the gated RMS norm on the
+ * layer's output fused into it (the oxydllm notes, "Performance": the Gated
+ * DeltaNet's gated norm runs as a fused kernel): instead of o it writes
+ *     y[t][h][j] = norm_weight[j] * o[t][h][j] / sqrt(mean_i o[t][h][i]^2 + eps)
+ *                  * silu(z[t][h][j]),   silu(a) = a / (1 + e^-a),
+ * the map of gdn_gated_rmsnorm, with o rounded to the problem's dtype first
+ * (what gdn_gated_rmsnorm would read).  For bf16 with chunk 32 or 64 the
+ * norm runs inside the carry kernel, so o never goes through memory; other
+ * problems run the carry into y and then the norm in place.  The result
+ * equals gdn_prefill_scan followed by gdn_gated_rmsnorm within rounding
+ * (the row sums are added in another order).
+ *
+ * z: [N_tok][H_v][d_v] in the problem's dtype, token stride stride_z
+ * (elements, >= H_v d_v, a multiple of 16 bytes), 16-byte aligned; the heads
+ * of a token are packed.  norm_weight: fp32 [d_v], shared by all heads.
+ * eps: finite, >= 0.  y: [N_tok][H_v][d_v] like o; it must not overlap z.
+ * Every other argument as gdn_prefill_scan; state_out is the carry's.
+ */
+gdn_status gdn_prefill_scan_gated_norm(const gdn_dims *d, const void *q, const void *k,
+                                      const void *v, const float *g, const float *beta,
+                                      const float *state_in, const int32_t *cu_seqlens,
+                                      const void *z, int64_t stride_z, const float *norm_weight,
+                                      float eps, void *y, float *state_out,
+                                      const void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_prefill_chunked with the gated norm fused as in
+ * gdn_prefill_scan_gated_norm: gdn_prefill_prepare followed by
+ * gdn_prefill_scan_gated_norm, both validated before anything is queued.
+ */
+gdn_status gdn_prefill_chunked_gated_norm(const gdn_dims *d, const void *q, const void *k,
+                                         const void *v, const float *g, const float *beta,
+                                         const float *state_in, const int32_t *cu_seqlens,
+                                         const void *z, int64_t stride_z,
+                                         const float *norm_weight, float eps, void *y,
+                                         float *state_out, void *workspace, size_t ws_bytes,
+                                         void *stream);
+
+/*
  * Convolution and prefill phase 1 in one call: the layer's short causal
  * conv1d + SiLU (Vallmo.jl README, "What's here") over the raw projected rows
  * x, whose channels are ordered [q | k | v] (C_conv = 2 H_k d_k + H_v d_v),

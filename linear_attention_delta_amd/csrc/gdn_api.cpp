@@ -290,6 +290,23 @@ gdn_status run_prepare(gdn::ScanArgs& a, hipStream_t s) {
 gdn_status run_scan(gdn::ScanArgs& a, const gdn_dims* d, hipStream_t s) {
   hipError_t e = gdn::launch_scan(a, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
+  if (a.norm_z && !gdn::seg_path(a) && d->total_tokens > 0) {
+    // the carry paths without the fused norm wrote o into y: the gated norm
+    // follows in place
+    gdn::NormArgs n;
+    n.rows = (long)d->total_tokens * d->num_v_heads;
+    n.heads = d->num_v_heads;
+    n.dv = d->head_dim_v;
+    n.dtype = d->dtype;
+    n.o = a.o;
+    n.z = a.norm_z;
+    n.weight = a.norm_w;
+    n.y = a.o;
+    n.stride_o = n.stride_y = (long)d->num_v_heads * d->head_dim_v;
+    n.stride_z = a.stride_z;
+    n.eps = a.norm_eps;
+    if ((e = gdn::launch_gated_norm(n, s)) != hipSuccess) return hip_fail(e, "gated norm launch");
+  }
   gdn_status st = debug_check(s, "o", a.o, (long)d->total_tokens * d->num_v_heads * d->head_dim_v, d->dtype);
   if (st != GDN_OK) return st;
   return debug_check(s, "state_out", a.state_out, (long)d->num_seqs * d->num_v_heads * d->head_dim_k * d->head_dim_v,
@@ -322,6 +339,33 @@ gdn_status scratch_of_current_device(void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+// The gated norm fused into the carry's output (NULL: plain o).
+struct NormIn {
+  const void* z;
+  int64_t stride_z;
+  const float* weight;
+  float eps;
+};
+
+gdn_status check_norm(const gdn_dims* d, const NormIn* n, const void* y) {
+  if (!n) return GDN_OK;
+  const int64_t row = (int64_t)d->num_v_heads * d->head_dim_v;
+  const int vec = d->dtype == GDN_BF16 ? 8 : 4;
+  if (n->stride_z < row || n->stride_z % vec)
+    return fail(GDN_ERR_INVALID_ARG, "stride_z must be >= H_v d_v (%lld) and a multiple of %d elements", (long long)row, vec);
+  if (!n->weight || !aligned(n->weight, 4)) return fail(GDN_ERR_INVALID_ARG, "norm weight must be non-NULL and 4-byte aligned");
+  if (!(n->eps >= 0.0f) || !std::isfinite(n->eps)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (d->total_tokens > 0) {
+    if (!n->z || !aligned(n->z, 16)) return fail(GDN_ERR_INVALID_ARG, "z must be non-NULL and 16-byte aligned");
+    const size_t esz = elem_size(d->dtype);
+    const size_t zb = ((size_t)(d->total_tokens - 1) * n->stride_z + row) * esz, yb = (size_t)d->total_tokens * row * esz;
+    const char* z0 = reinterpret_cast<const char*>(n->z);
+    const char* y0 = reinterpret_cast<const char*>(y);
+    if (y0 && z0 < y0 + yb && y0 < z0 + zb) return fail(GDN_ERR_INVALID_ARG, "y must not overlap z");
+  }
   return GDN_OK;
 }
 
@@ -428,9 +472,11 @@ gdn_status gdn_prefill_prepare(const gdn_dims* d, const void* q, const void* k, 
 // (the carry kernels read neither g nor beta)
 static gdn_status scan_impl(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* state_in, const int32_t* cu_seqlens, void* o,
-                            float* state_out, const void* workspace, size_t ws_bytes, void* stream, bool need_gb) {
+                            float* state_out, const void* workspace, size_t ws_bytes, void* stream, bool need_gb,
+                            const NormIn* norm = nullptr) {
   gdn_status st = check_dims(d, 0);
   if (st != GDN_OK) return st;
+  if ((st = check_norm(d, norm, o)) != GDN_OK) return st;
   if ((st = check_scan_ptrs(d, q, k, v, g, beta, cu_seqlens, true, need_gb)) != GDN_OK) return st;
   if ((st = check_workspace(d, workspace, ws_bytes)) != GDN_OK) return st;
   if (d->total_tokens > 0 && (!o || !aligned(o, 16))) return fail(GDN_ERR_INVALID_ARG, "o must be non-NULL and 16-byte aligned");
@@ -447,6 +493,12 @@ static gdn_status scan_impl(const gdn_dims* d, const void* q, const void* k, con
   a.cu_seqlens = cu_seqlens;
   a.o = o;
   a.state_out = state_out;
+  if (norm) {
+    a.norm_z = norm->z;
+    a.stride_z = norm->stride_z;
+    a.norm_w = norm->weight;
+    a.norm_eps = norm->eps;
+  }
   carve(a, d, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = run_scan(a, d, s)) != GDN_OK) return st;
@@ -501,6 +553,29 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* q, const v
   void* ws = nullptr;
   if ((st = scratch_of_current_device(&ws)) != GDN_OK) return st;
   return gdn_prefill_chunked(d, q, k, v, g, beta, state_in, cu_seqlens, o, state_out, ws, kScratchBytes, stream);
+}
+
+gdn_status gdn_prefill_scan_gated_norm(const gdn_dims* d, const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const float* state_in, const int32_t* cu_seqlens,
+                                      const void* z, int64_t stride_z, const float* norm_weight, float eps, void* y,
+                                      float* state_out, const void* workspace, size_t ws_bytes, void* stream) {
+  const NormIn n{z, stride_z, norm_weight, eps};
+  return scan_impl(d, q, k, v, g, beta, state_in, cu_seqlens, y, state_out, workspace, ws_bytes, stream, true, &n);
+}
+
+gdn_status gdn_prefill_chunked_gated_norm(const gdn_dims* d, const void* q, const void* k, const void* v,
+                                         const float* g, const float* beta, const float* state_in,
+                                         const int32_t* cu_seqlens, const void* z, int64_t stride_z,
+                                         const float* norm_weight, float eps, void* y, float* state_out,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+  // both halves validated before the prepare is queued
+  gdn_status st = validate_prefill(d, q, k, v, g, beta, state_in, cu_seqlens, y, state_out, workspace, ws_bytes);
+  if (st != GDN_OK) return st;
+  const NormIn n{z, stride_z, norm_weight, eps};
+  if ((st = check_norm(d, &n, y)) != GDN_OK) return st;
+  if ((st = gdn_prefill_prepare(d, q, k, g, beta, cu_seqlens, workspace, ws_bytes, stream)) != GDN_OK) return st;
+  return gdn_prefill_scan_gated_norm(d, q, k, v, g, beta, state_in, cu_seqlens, z, stride_z, norm_weight, eps, y,
+                                     state_out, workspace, ws_bytes, stream);
 }
 
 static gdn_status conv_prepare_impl(const gdn_dims* d, const gdn_gate_inputs* gates, int32_t conv_width,

@@ -146,6 +146,35 @@ struct Stager {
   long sk, sq, sv, mstep, sstep;
   int ntok, tid, l2norm;
   float scale;
+  // the fused norm's gate rows z, staged like V (in V's buffer once the
+  // carry is done with V)
+  u32x4 rz[OUT ? NV : 1];
+  long zoff[OUT ? NV : 1];
+  const uint16_t* zp;
+
+  __device__ __forceinline__ void setup_z(const uint16_t* z, long stride_z) {
+    zp = z;
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + NTH * j, r = idx / (DV / 8), cv = idx % (DV / 8);
+      zoff[j] = (long)r * stride_z + 8 * cv;
+    }
+  }
+  __device__ __forceinline__ void zload(int ch, long stride_z) {
+    const int cs = ch * C;
+    const int clen = min(C, ntok - cs);
+    const uint16_t* zc = zp + (long)cs * stride_z;
+#pragma unroll
+    for (int j = 0; j < NV; j++)
+      rz[j] = vrow[j] < clen ? *reinterpret_cast<const u32x4*>(zc + zoff[j]) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ void zstore(SM& sm, int b) const {
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int idx = tid + NTH * j, r = idx / (DV / 8), cv = idx % (DV / 8);
+      if (idx < VV) *reinterpret_cast<u32x4*>(&sm.v[b][r][8 * cv]) = rz[j];
+    }
+  }
 
   __device__ __forceinline__ void setup_offsets() {
 #pragma unroll
@@ -687,13 +716,26 @@ __global__ void __launch_bounds__(64 * (CW * RS + LW)) k_seg_combine(ScanArgs a)
 // outputs, 4..7 stage the chunks and form each chunk's P while the carry
 // works up to its last product, which waits for P at a second barrier.  The staging registers live only
 // in the staging waves, so the carry keeps its accumulators in VGPRs.
-template <int C, int DK, int DV, int NCW>
+//
+// NORM: the gated RMS norm is applied to o before it is written (the
+// oxydllm notes, "Performance": the gated norm runs fused): each (token,
+// v-head) row becomes y = w * o / sqrt(mean(o^2) + eps) * silu(z), with o
+// rounded to bf16 first, as the separate kernel reads it.  A row's 128
+// columns belong to the four carry waves, so each wave adds up the squares
+// of its columns per token and leaves them in LDS (double-buffered by chunk
+// parity); the next chunk's first barrier publishes them, and the rows are
+// finished while the carry waves wait for the next chunk's P.  A chunk's o
+// stays in registers (bf16) until then; the staging waves load its gate
+// rows a chunk ahead and leave them in the chunk's V buffer, which the
+// carry no longer reads after the chunk's P barrier.
+template <int C, int DK, int DV, int NCW, bool NORM>
 __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   typedef SegSmem<C, DK, DV, true> SM;
   constexpr int NDT = DK / 16;
   constexpr int NCT = DV / (16 * NCW);  // state column tiles per carry wave
   static_assert(NCT * 16 * NCW == DV, "state columns must split over the carry waves");
   __shared__ SM sm;
+  __shared__ float nss[NORM ? 2 * NCW * C : 1];  // [parity][carry wave][token]: row sums of o^2
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = 4 * (lane >> 4);
   int n, hk, h;
@@ -709,18 +751,30 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
     // the carry waves work on chunk i
     Stager<C, DK, DV, true, 256> st;
     init_stager(st, a, sg, hk, h, tid - 64 * NCW);
+    if constexpr (NORM)
+      st.setup_z(reinterpret_cast<const uint16_t*>(a.norm_z) + (long)sg.s0 * a.stride_z + (long)h * DV, a.stride_z);
     if (nch > 0) {
       st.load(ch0);
       st.setup_tt(sm);
       st.store(sm, 0);
       if (nch > 1) st.load(ch0 + 1);
+      if constexpr (NORM) st.zload(ch0, a.stride_z);
     }
     for (int i = 0; i < nch; i++) {
       lds_barrier();
       compute_p<C, DK, DV, 4>(sm, i & 1, wave - NCW, lane);
       lds_barrier();  // P ready for the carry's last product
+      // NORM: chunk i's gate rows into its V buffer, which the carry no
+      // longer reads; the carry waves use them after the next barrier
+      if constexpr (NORM) st.zstore(sm, i & 1);
       if (i + 1 < nch) st.store(sm, (i + 1) & 1);
       if (i + 2 < nch) st.load(ch0 + i + 2);
+      if constexpr (NORM) {
+        if (i + 1 < nch) st.zload(ch0 + i + 1, a.stride_z);
+      }
+    }
+    if constexpr (NORM) {
+      if (nch > 0) lds_barrier();  // publishes the last chunk's row sums and gate rows
     }
     return;
   }
@@ -744,10 +798,10 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   }
   const long orow = (long)a.hv * DV;
   uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)sg.s0 * orow + (long)h * DV;
-  u32x2 ob[NCT][C / 16];
-  for (int i = 0; i < nch; i++) {
-    lds_barrier();
-    carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob, [] { lds_barrier(); });
+  // o (or y) rows of chunk i of this segment, NCT tiles of bf16 in the
+  // output layout: lane (c16, g) holds columns 4g..4g+3 of tile j for token
+  // 16t + c16
+  auto store_rows = [&](int i, const u32x2 (&rows)[NCT][C / 16]) {
     const int cs = (ch0 + i) * C;
     const int clen = min(C, sg.s1 - sg.s0 - cs);
     uint16_t* oc = obase + (long)cs * orow;
@@ -758,16 +812,90 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
         // lanes g and g^1 (16 apart) trade halves so that each writes 8
         // adjacent columns: even g the first tile, odd g the second
         const bool ev = ((lane >> 4) & 1) == 0;
-        const u32x2 send = ev ? ob[1][t] : ob[0][t];
+        const u32x2 send = ev ? rows[1][t] : rows[0][t];
         const u32x2 recv = {(uint32_t)__shfl_xor((int)send[0], 16, 64), (uint32_t)__shfl_xor((int)send[1], 16, 64)};
-        const u32x4 w = ev ? u32x4{ob[0][t][0], ob[0][t][1], recv[0], recv[1]}
-                           : u32x4{recv[0], recv[1], ob[1][t][0], ob[1][t][1]};
+        const u32x4 w = ev ? u32x4{rows[0][t][0], rows[0][t][1], recv[0], recv[1]}
+                           : u32x4{recv[0], recv[1], rows[1][t][0], rows[1][t][1]};
         const int col = ev ? vcol[0] + r4 : vcol[1] + r4 - 4;
         if (tok < clen) *reinterpret_cast<u32x4*>(oc + (long)tok * orow + col) = w;
       } else if (tok < clen) {
 #pragma unroll
-        for (int j = 0; j < NCT; j++) *reinterpret_cast<u32x2*>(oc + (long)tok * orow + vcol[j] + r4) = ob[j][t];
+        for (int j = 0; j < NCT; j++) *reinterpret_cast<u32x2*>(oc + (long)tok * orow + vcol[j] + r4) = rows[j][t];
       }
+    }
+  };
+  u32x2 ob[NCT][C / 16];
+  if constexpr (!NORM) {
+    for (int i = 0; i < nch; i++) {
+      lds_barrier();
+      carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob, [] { lds_barrier(); });
+      store_rows(i, ob);
+    }
+  } else {
+    // the fused gated norm (see above); the previous chunk's o in obp, the
+    // weights of this lane's columns in wn
+    u32x2 obp[NCT][C / 16];
+    float wn[NCT][4];
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) wn[j][e] = a.norm_w[vcol[j] + r4 + e];
+    // this wave's part of each row's sum of squares -> LDS slot of the parity
+    auto row_sums = [&](int i) {
+#pragma unroll
+      for (int t = 0; t < C / 16; t++) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCT; j++) {
+          const f32x4 o4 = bf4_to_f32(ob[j][t]);
+#pragma unroll
+          for (int e = 0; e < 4; e++) ss += o4[e] * o4[e];
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < 16) nss[((i & 1) * NCW + wave) * C + 16 * t + c16] = ss;
+      }
+    };
+    // y of chunk i from obp, the published row sums and the gate rows the
+    // staging waves left in the chunk's V buffer; y overwrites obp
+    auto finish = [&](int i) {
+#pragma unroll
+      for (int t = 0; t < C / 16; t++) {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < NCW; w++) ss += nss[((i & 1) * NCW + w) * C + 16 * t + c16];
+        const float inv_rms = 1.0f / sqrtf(ss * (1.0f / DV) + a.norm_eps);
+#pragma unroll
+        for (int j = 0; j < NCT; j++) {
+          const f32x4 o4 = bf4_to_f32(obp[j][t]);
+          const f32x4 z4 = bf4_to_f32(*reinterpret_cast<const u32x2*>(&sm.v[i & 1][16 * t + c16][vcol[j] + r4]));
+          f32x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            y[e] = wn[j][e] * o4[e] * inv_rms *
+                   (z4[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z4[e] * 1.44269504088896341f)));
+          obp[j][t] = pack4_bf16(y);
+        }
+      }
+      store_rows(i, obp);
+    };
+    for (int i = 0; i < nch; i++) {
+      lds_barrier();  // also publishes chunk i-1's row sums
+      carry_chunk<C, DK, DV, NCT, true>(sm, i & 1, Z, vcol, lane, ob, [&] {
+        // in the wait for P: the previous chunk's rows are finished (its
+        // gate rows come from LDS; only its o stays live across the carry)
+        if (i > 0) finish(i - 1);
+        lds_barrier();
+      });
+      row_sums(i);
+#pragma unroll
+      for (int j = 0; j < NCT; j++)
+#pragma unroll
+        for (int t = 0; t < C / 16; t++) obp[j][t] = ob[j][t];
+    }
+    if (nch > 0) {
+      lds_barrier();
+      finish(nch - 1);
     }
   }
 
@@ -808,7 +936,8 @@ hipError_t launch_seg_t(const ScanArgs& a, hipStream_t s) {
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   constexpr int NCW = kPass2CarryWaves * 16 <= DV ? kPass2CarryWaves : DV / 16;
-  hipLaunchKernelGGL((k_seg_pass2<C, DK, DV, NCW>), grid, dim3(64 * (NCW + 4)), 0, s, a);
+  if (a.norm_z) hipLaunchKernelGGL((k_seg_pass2<C, DK, DV, NCW, true>), grid, dim3(64 * (NCW + 4)), 0, s, a);
+  else hipLaunchKernelGGL((k_seg_pass2<C, DK, DV, NCW, false>), grid, dim3(64 * (NCW + 4)), 0, s, a);
   return hipGetLastError();
 }
 

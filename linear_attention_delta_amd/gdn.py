@@ -30,7 +30,8 @@ EXPORTED = ["gdn_status_string", "gdn_last_error", "gdn_version", "gdn_validate_
             "gdn_prefill_scan",
             "gdn_prefill_conv_prepare", "gdn_prefill_conv_chunked", "gdn_decode_step", "gdn_decode_conv_step",
             "gdn_gated_rmsnorm", "gdn_gating", "gdn_prefill_conv_gated", "gdn_decode_conv_gated_step",
-            "gdn_snapshot_push", "gdn_snapshot_restore"]
+            "gdn_snapshot_push", "gdn_snapshot_restore", "gdn_prefill_scan_gated_norm",
+            "gdn_prefill_chunked_gated_norm"]
 
 
 class GdnDims(ctypes.Structure):
@@ -84,6 +85,8 @@ def _load():
         "gdn_prefill_conv_gated": ([D, GI, i32, P, i64, P, P, P, P, P, P, i64, P, P, P, sz, P], i32),
         "gdn_decode_conv_gated_step": ([D, GI, i32, P, i64, P, P, P, P, i32, P, P, P], i32),
         "gdn_snapshot_push": ([i32, P, i32, i64, P, i64, P, i32, P, P, P, P], i32),
+        "gdn_prefill_scan_gated_norm": ([D, P, P, P, P, P, P, P, P, i64, P, ctypes.c_float, P, P, P, sz, P], i32),
+        "gdn_prefill_chunked_gated_norm": ([D, P, P, P, P, P, P, P, P, i64, P, ctypes.c_float, P, P, P, sz, P], i32),
         "gdn_snapshot_restore": ([i32, P, i32, i64, P, i64, P, i32, P, P, i32, P], i32),
     }
     for name, (args, res) in sig.items():
@@ -269,6 +272,23 @@ class Prefill:
                                        _ptr(state_in), _ptr(self.cu_seqlens), _ptr(o), _ptr(state_out),
                                        _ptr(self.ws), self.ws_bytes, _stream(stream)))
 
+    def gated_norm(self, q, k, v, g, beta, z, norm_weight, y, state_in=None, state_out=None, eps=1e-6,
+                   stream=None):
+        """The prefill with the gated norm fused (gdn_prefill_chunked_gated_norm):
+        y [N_tok, H_v, d_v] = weight * o / rms(o) * silu(z) instead of o."""
+        _check(lib.gdn_prefill_chunked_gated_norm(
+            ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(self.cu_seqlens), _ptr(z), _row_stride(z), _ptr(norm_weight), ctypes.c_float(eps), _ptr(y),
+            _ptr(state_out), _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def scan_gated_norm(self, q, k, v, g, beta, z, norm_weight, y, state_in=None, state_out=None, eps=1e-6,
+                        stream=None):
+        """The carry half with the gated norm fused (gdn_prefill_scan_gated_norm)."""
+        _check(lib.gdn_prefill_scan_gated_norm(
+            ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(self.cu_seqlens), _ptr(z), _row_stride(z), _ptr(norm_weight), ctypes.c_float(eps), _ptr(y),
+            _ptr(state_out), _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
 
 def prefill(q, k, v, g, beta, *, state_in=None, cu_seqlens=None, seqlen=None, num_seqs=None, chunk_size=64,
             l2norm=True, heads_tiled=False, scale=1.0, want_state=True, out=None, state_out=None, stream=None):
@@ -353,6 +373,16 @@ class ConvPrefill:
         _check(lib.gdn_prefill_scan(ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                     _ptr(state_in), _ptr(self.cu_seqlens), _ptr(o), _ptr(state_out),
                                     _ptr(self.ws), self.ws_bytes, _stream(stream)))
+
+    def scan_gated_norm(self, y, g, beta, z, norm_weight, out, state_in=None, state_out=None, eps=1e-6,
+                        stream=None):
+        """The carry on the q, k, v column blocks of the conv output y, with
+        the gated norm fused: out = weight * o / rms(o) * silu(z)."""
+        q, k, v = self.views(y)
+        _check(lib.gdn_prefill_scan_gated_norm(
+            ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(self.cu_seqlens), _ptr(z), _row_stride(z), _ptr(norm_weight), ctypes.c_float(eps), _ptr(out),
+            _ptr(state_out), _ptr(self.ws), self.ws_bytes, _stream(stream)))
 
     def __call__(self, x, y, g, beta, o, state_in=None, state_out=None, conv_state=None, stream=None):
         _check(lib.gdn_prefill_conv_chunked(ctypes.byref(self.dims), self.width, _ptr(x), _row_stride(x),
