@@ -301,8 +301,13 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
   }
 }
 
-constexpr int kConvTok = 8;  // rows per block
-constexpr int kConvRun = 2;  // blocks per thread: one halo per 16 rows, block 2 loads in flight during block 1
+// rows per block and blocks per thread (one halo per 16 rows; the next
+// block's loads in flight while a block is computed).  At the 4096-token
+// layer: 4 x 4 34.6 us, 8 x 2 35.4, 2 x 8 34.9, 4 x 3 37.9, 4 x 2 40.0,
+// 8 x 1 40.2, 2 x 4 42.0, 8 x 4 50.2, 2 x 2 52.2, 8 x 8 82.3 (fewer, longer
+// threads keep less in flight per byte moved).
+constexpr int kConvTok = 4;
+constexpr int kConvRun = 4;
 
 template <class E, int W>
 hipError_t launch_w(const ConvArgs& a, hipStream_t s) {

@@ -168,3 +168,54 @@ def test_silu_bf16_pre_activation_sweep(G, orc):
     ref = orc.conv1d_f32(x, w, np.array([0, 2], dtype=np.int32), out_bf16=True)[1]
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, f"{bad.size} mismatches, first a={a[bad[0]]!r}: got {got[bad[0]]:#06x} want {ref[bad[0]]:#06x}"
+
+
+@pytest.mark.slow
+def test_silu_bf16_every_fp32_preactivation(G, orc):
+    """Every fp32 pre-activation, through the bf16 convolution kernel: with
+    all taps zero the pre-activation is exactly the channel's fp32 bias
+    (fma(0, 0, b) = b), so 1024 launches of 2^22 channels, each channel's
+    bias one of the 2^32 bit patterns, give SiLU rounded to bf16 for every
+    fp32 value -- on the kernel's general path (first rows of the sequence)
+    and on its fast path (rows whose window lies inside the sequence).  Each
+    must equal the oracle's fp32 definition (Cody-Waite exponential, exact
+    division, round to nearest even) bit for bit; the test stops at the
+    first launch with a mismatch and names its input.  About 16 s on one
+    MI355X with 16 host threads for the oracle."""
+    import threading
+
+    import torch
+    C, T, NBLK = 1 << 22, 32, 1 << 10
+    x = torch.zeros((T, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((C, 4), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    conv = G.Conv1d(x, w, seqlen=T)
+    x1 = np.zeros((1, C), dtype=np.float32)
+    w1 = np.zeros((C, 4), dtype=np.float32)
+    cu1 = np.array([0, 1], dtype=np.int32)
+    n_thr = 16
+    for blk in range(NBLK):
+        a = (np.arange(C, dtype=np.uint64) + np.uint64(blk) * np.uint64(C)).astype(np.uint32).view(np.float32)
+        bias = torch.from_numpy(a).cuda()
+        conv = G.Conv1d(x, w, seqlen=T, bias=bias)
+        conv(x, y)
+        got = _bits(y[[0, T // 2]])
+        ref = np.empty(C, dtype=np.uint16)
+
+        def part(i):
+            s = slice(i * C // n_thr, (i + 1) * C // n_thr)
+            ref[s] = orc.conv1d_f32(x1[:, s], w1[s], cu1, bias=a[s], out_bf16=True)[0]
+
+        th = [threading.Thread(target=part, args=(i,)) for i in range(n_thr)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        for row in (0, 1):
+            bad = np.flatnonzero(got[row] != ref)
+            assert bad.size == 0, (f"block {blk}, row {'general' if row == 0 else 'fast'} path: {bad.size} "
+                                   f"mismatches, first a bits {a.view(np.uint32)[bad[0]]:#010x}: "
+                                   f"got {got[row][bad[0]]:#06x} want {ref[bad[0]]:#06x}")
+        if blk % 64 == 0:
+            note(f"  exhaustive SiLU: {blk + 1} of {NBLK} blocks of 2^22 inputs match")
+    note("  exhaustive SiLU: all 2^32 fp32 pre-activations match")
