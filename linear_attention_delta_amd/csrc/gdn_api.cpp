@@ -185,11 +185,16 @@ gdn_status hip_fail(hipError_t e, const char* what) {
   return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// ---- GDN_DEBUG probe: the count lives in a file-scope device variable.
+// ---- GDN_DEBUG probe: the count lives in a file-scope device variable (one
+// per device).  A probe zeroes it, counts into it and reads it back, then
+// synchronises its stream; probes from several host threads (on any
+// streams) take turns under a mutex, so no probe sees another's count.
 __device__ int g_nonfinite_count;
+std::mutex g_debug_mu;
 
 gdn_status debug_check(hipStream_t s, const char* what, const void* p, long n, int dtype) {
   if (!debug_enabled() || !p || n <= 0) return GDN_OK;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
   int* dcount = nullptr;
   hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&dcount), HIP_SYMBOL(g_nonfinite_count));
   if (e != hipSuccess) return hip_fail(e, "GDN_DEBUG symbol");
