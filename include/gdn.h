@@ -168,8 +168,9 @@ gdn_status gdn_validate(const gdn_dims *d, int32_t op, const void *const *ptrs, 
  * with stride stride_y (>= C).  weight: fp32 [C][W]; bias: fp32 [C] or NULL.
  * conv_state: [N][W-1][C] in dtype, in/out, or NULL: on return it holds the
  * last W-1 raw inputs of (old window ++ sequence), ready for the next call.
- * x and y must not overlap.  A sequence with zero tokens leaves its window
- * unchanged.  With seqlen == 1 this is the decode-time conv step.
+ * x, y and conv_state must not overlap one another (GDN_ERR_INVALID_ARG).
+ * A sequence with zero tokens leaves its window unchanged.  With
+ * seqlen == 1 this is the decode-time conv step.
  */
 gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen,
                       const int32_t *cu_seqlens, int32_t channels, int32_t width,

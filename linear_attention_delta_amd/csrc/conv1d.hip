@@ -85,24 +85,40 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
   // contiguous run of token spans (all channel blocks of each), i.e. one
   // contiguous stretch of rows, so the W-1 halo rows a span reads were
   // fetched into that XCD's L2 by its predecessor.
-  const int ntb = (a.total_tokens + SPAN - 1) / SPAN;
-  const int ncb = gridDim.x / ntb;  // channel blocks
+  // Channel blocks of 256 groups (the launch's block size); with a power of
+  // two of them (8192 channels: 4) the index splits by shifts, since an
+  // integer division here delays every address, hence every first load.
+  const int ncb = (a.channels / V + 255) >> 8;
   int L = blockIdx.x;
   if ((gridDim.x & 7) == 0) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int cg = (L % ncb) * blockDim.x + threadIdx.x;  // channel group
+  int span_idx, cb;
+  if ((ncb & (ncb - 1)) == 0) {
+    span_idx = L >> __builtin_ctz(ncb);
+    cb = L & (ncb - 1);
+  } else {
+    span_idx = L / ncb;
+    cb = L - span_idx * ncb;
+  }
+  const int cg = cb * 256 + threadIdx.x;  // channel group
   const int c0 = cg * V;
   if (c0 >= a.channels) return;
-  const int t_begin = (L / ncb) * SPAN;
+  const int t_begin = span_idx * SPAN;
   if (t_begin >= a.total_tokens) return;
   const int t_end = min(t_begin + SPAN, a.total_tokens);
 
+  // Every load below is unconditional: an optional operand is read from a
+  // valid stand-in address and masked to +0 afterwards.  A load inside a
+  // branch makes the compiler drain all loads in flight where the branch
+  // rejoins, i.e. one full memory round trip per optional operand.
   float w[V][W];
   float bias[V];
+  const float* bsrc = a.bias ? a.bias : a.weight;
+  const uint32_t bmask = a.bias ? ~0u : 0u;
 #pragma unroll
   for (int i = 0; i < V; i++) {
 #pragma unroll
     for (int j = 0; j < W; j++) w[i][j] = a.weight[(long)(c0 + i) * W + j];
-    bias[i] = a.bias ? a.bias[c0 + i] : 0.0f;
+    bias[i] = __uint_as_float(__float_as_uint(bsrc[c0 + i]) & bmask);
   }
   const T* x = reinterpret_cast<const T*>(a.x);
   T* y = reinterpret_cast<T*>(a.y);
@@ -110,7 +126,7 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
 
   int seq, seq_start, seq_end;
   if (a.seqlen > 0) {
-    seq = t_begin / a.seqlen;
+    seq = a.num_seqs == 1 ? 0 : t_begin / a.seqlen;
     seq_start = seq * a.seqlen;
     seq_end = seq_start + a.seqlen;
   } else {
@@ -119,17 +135,36 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
     seq_end = a.cu_seqlens[seq + 1];
   }
 
-  // Fast path: the span and its W-1 token halo lie inside one sequence.  The
-  // span is walked in RUN blocks of TOK rows; the rows of block r + 1 are in
-  // flight while block r is computed, and the last W inputs stay converted
-  // to fp32 in a sliding register window, so no row is read twice.
-  if (t_end - t_begin == SPAN && t_begin - (W - 1) >= seq_start && t_end <= seq_end) {
-    typedef typename Vec<E>::raw_t raw_t;
+  // Fast path: a span inside one sequence.  The span is walked in RUN
+  // blocks of TOK rows; the rows of block r + 1 are in flight while block r
+  // is computed, and the last W inputs stay converted to fp32 in a sliding
+  // register window, so no row is read twice.  Halo rows before the
+  // sequence's first token come from its window (or are zero).  Spans at a
+  // sequence start and the ragged last span take this path too: the grid is
+  // resident all at once, so a workgroup on the token-by-token path below
+  // would set the kernel's duration.  The ragged span runs its own copy of
+  // the walk (RAGGED: row addresses clamped into the span, rows past its end
+  // computed and not stored); in the full span's code the guards cost
+  // 2.5 us at the 4096-token layer.
+  typedef typename Vec<E>::raw_t raw_t;
+  auto walk = [&](auto ragged) {
+    constexpr bool RAGGED = decltype(ragged)::value;
+    auto row_at = [&](int t) { return RAGGED ? min(t, t_end - 1) : t; };
     raw_t halo[W - 1], cur[TOK];
 #pragma unroll
-    for (int j = 0; j < W - 1; j++) halo[j] = Vec<E>::load_raw(x + (long)(t_begin - (W - 1) + j) * a.stride_x + c0);
+    for (int j = 0; j < W - 1; j++) {
+      // from x inside the sequence, else slot (W-1) + (pos - seq_start) of
+      // the sequence's window, else zero (a row of x read and masked)
+      const int pos = t_begin - (W - 1) + j;
+      const bool in_seq = pos >= seq_start;
+      const T* src = in_seq ? x + (long)pos * a.stride_x + c0
+                     : win  ? win + ((long)seq * (W - 1) + (W - 1) + (pos - seq_start)) * a.channels + c0
+                            : x + (long)t_begin * a.stride_x + c0;
+      halo[j] = Vec<E>::load_raw(src);
+      if (!in_seq && !win) halo[j] = raw_t{};
+    }
 #pragma unroll
-    for (int j = 0; j < TOK; j++) cur[j] = Vec<E>::load_raw(x + (long)(t_begin + j) * a.stride_x + c0);
+    for (int j = 0; j < TOK; j++) cur[j] = Vec<E>::load_raw(x + (long)row_at(t_begin + j) * a.stride_x + c0);
     float wv[W][V];
 #pragma unroll
     for (int j = 0; j < W - 1; j++) Vec<E>::cvt(halo[j], wv[j]);
@@ -139,7 +174,7 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
       if (r + 1 < RUN) {
 #pragma unroll
         for (int j = 0; j < TOK; j++)
-          nxt[j] = Vec<E>::load_raw(x + (long)(t_begin + (r + 1) * TOK + j) * a.stride_x + c0);
+          nxt[j] = Vec<E>::load_raw(x + (long)row_at(t_begin + (r + 1) * TOK + j) * a.stride_x + c0);
       }
 #pragma unroll
       for (int tt = 0; tt < TOK; tt++) {
@@ -154,11 +189,12 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
           if constexpr (ACT && std::is_same<E, BF16>::value) out[i] = conv_sum<W>(bias[i], w[i], xv);
           else out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
         }
+        const bool keep = !RAGGED || t_begin + p < t_end;
         if constexpr (ACT && std::is_same<E, BF16>::value) {
           silu8_for_bf16(out);
-          *reinterpret_cast<u32x4*>(y + (long)(t_begin + p) * a.stride_y + c0) = conv_pack_bf16x8_canonical(out);
+          if (keep) *reinterpret_cast<u32x4*>(y + (long)(t_begin + p) * a.stride_y + c0) = conv_pack_bf16x8_canonical(out);
         } else {
-          Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
+          if (keep) Vec<E>::store(y + (long)(t_begin + p) * a.stride_y + c0, out);
         }
       }
       if (r + 1 < RUN) {
@@ -166,56 +202,77 @@ __global__ void __launch_bounds__(256) k_conv1d(ConvArgs a) {
         for (int j = 0; j < TOK; j++) cur[j] = nxt[j];
       }
     }
+  };
+  if (t_end <= seq_end) {
+    if (t_end - t_begin == SPAN) walk(std::false_type{});
+    else walk(std::true_type{});
     return;
   }
 
-  // General path (sequence starts inside the block): walk token by token.
+  // General path (a sequence starts inside the span).  Rows are fetched TOK
+  // at a time, the next block's in flight while a block runs, each address
+  // clamped into the span so that no load sits in a branch; tokens then run
+  // one by one, and a sequence start reloads that sequence's context.
   // hist[j] = input at position t - (W-1) + j for the token t about to run
+  typedef typename Vec<E>::raw_t raw_t;
   float hist[W][V];
-  auto fill_context = [&](int t) {
+  auto fill_context = [&](int t) {  // positions t-(W-1) .. t-1 of sequence seq
 #pragma unroll
     for (int j = 0; j < W - 1; j++) {
-      int pos = t - (W - 1) + j;  // absolute token index
-      if (pos >= seq_start) {
-        Vec<E>::load(x + (long)pos * a.stride_x + c0, hist[j]);
-      } else if (win) {
-        int slot = (W - 1) + (pos - seq_start);  // 0..W-2, W-2 newest
-        Vec<E>::load(win + ((long)seq * (W - 1) + slot) * a.channels + c0, hist[j]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; i++) hist[j][i] = 0.0f;
-      }
+      const int pos = t - (W - 1) + j;
+      const bool in_seq = pos >= seq_start;
+      const T* src = in_seq ? x + (long)pos * a.stride_x + c0
+                     : win  ? win + ((long)seq * (W - 1) + (W - 1) + (pos - seq_start)) * a.channels + c0
+                            : x + (long)t * a.stride_x + c0;
+      raw_t v = Vec<E>::load_raw(src);
+      if (!in_seq && !win) v = raw_t{};
+      Vec<E>::cvt(v, hist[j]);
     }
   };
+  auto row = [&](int t) { return Vec<E>::load_raw(x + (long)min(t, t_end - 1) * a.stride_x + c0); };
+  raw_t rows[TOK];
+#pragma unroll
+  for (int j = 0; j < TOK; j++) rows[j] = row(t_begin + j);
   fill_context(t_begin);
 
-  for (int t = t_begin; t < t_end; t++) {
-    if (t == seq_end) {  // next sequence: fresh context
-      seq++;
-      if (a.seqlen > 0) {
-        seq_start = t;
-        seq_end = t + a.seqlen;
-      } else {
-        while (a.cu_seqlens[seq + 1] <= t) seq++;  // skip empty sequences
-        seq_start = a.cu_seqlens[seq];
-        seq_end = a.cu_seqlens[seq + 1];
+  for (int tb = t_begin; tb < t_end; tb += TOK) {
+    raw_t nrows[TOK];
+#pragma unroll
+    for (int j = 0; j < TOK; j++) nrows[j] = row(tb + TOK + j);
+#pragma unroll
+    for (int j = 0; j < TOK; j++) {
+      const int t = tb + j;
+      if (t < t_end) {
+        if (t == seq_end) {  // next sequence: fresh context
+          seq++;
+          if (a.seqlen > 0) {
+            seq_start = t;
+            seq_end = t + a.seqlen;
+          } else {
+            while (a.cu_seqlens[seq + 1] <= t) seq++;  // skip empty sequences
+            seq_start = a.cu_seqlens[seq];
+            seq_end = a.cu_seqlens[seq + 1];
+          }
+          fill_context(t);
+        }
+        Vec<E>::cvt(rows[j], hist[W - 1]);
+        float out[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+          float xv[W];
+#pragma unroll
+          for (int k = 0; k < W; k++) xv[k] = hist[k][i];
+          out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
+        }
+        Vec<E>::store(y + (long)t * a.stride_y + c0, out);
+#pragma unroll
+        for (int k = 0; k < W - 1; k++)
+#pragma unroll
+          for (int i = 0; i < V; i++) hist[k][i] = hist[k + 1][i];
       }
-      fill_context(t);
     }
-    Vec<E>::load(x + (long)t * a.stride_x + c0, hist[W - 1]);
-    float out[V];
 #pragma unroll
-    for (int i = 0; i < V; i++) {
-      float xv[W];
-#pragma unroll
-      for (int j = 0; j < W; j++) xv[j] = hist[j][i];
-      out[i] = conv_point<E, W, ACT>(bias[i], w[i], xv);
-    }
-    Vec<E>::store(y + (long)t * a.stride_y + c0, out);
-#pragma unroll
-    for (int j = 0; j < W - 1; j++)
-#pragma unroll
-      for (int i = 0; i < V; i++) hist[j][i] = hist[j + 1][i];
+    for (int j = 0; j < TOK; j++) rows[j] = nrows[j];
   }
 }
 
@@ -303,9 +360,12 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
 
 // rows per block and blocks per thread (one halo per 16 rows; the next
 // block's loads in flight while a block is computed).  At the 4096-token
-// layer: 4 x 4 34.6 us, 8 x 2 35.4, 2 x 8 34.9, 4 x 3 37.9, 4 x 2 40.0,
-// 8 x 1 40.2, 2 x 4 42.0, 8 x 4 50.2, 2 x 2 52.2, 8 x 8 82.3 (fewer, longer
-// threads keep less in flight per byte moved).
+// layer (bf16, 8192 channels, N(0, 1) inputs, one call after another):
+// 4 x 4 28.9 us, 4 x 8 31.9.  With the exact SiLU branch never taken
+// (constant inputs) 4 x 8 led: 25.7 against 26.6, then 2 x 8 27.2,
+// 4 x 16 27.0, 8 x 4 28.5, 8 x 2 28.6, 2 x 16 29.2, 4 x 2 32.0, 8 x 1 32.1,
+// 2 x 4 33.7; with real data the kernel is near VALU-bound and the four
+// workgroups per CU of 4 x 4 hide more of it.
 constexpr int kConvTok = 4;
 constexpr int kConvRun = 4;
 

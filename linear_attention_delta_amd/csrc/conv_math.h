@@ -62,17 +62,19 @@ __device__ __forceinline__ float silu_fast(float a) {
 // input: the fast form for all eight, then one (rarely taken) branch that
 // redoes the flagged ones exactly, instead of a branch per element.
 __device__ __forceinline__ void silu8_for_bf16(float (&v)[8]) {
+  // m: which of the eight need the exact form, kept as bits so that the
+  // (often taken: any of 64 lanes may ask) branch does not test them again
   float q[8];
-  bool any = false;
+  uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     q[i] = silu_fast(v[i]);
-    any |= silu_needs_exact(v[i], q[i]);
+    m |= silu_needs_exact(v[i], q[i]) ? 1u << i : 0u;
   }
-  if (any) {
+  if (m) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      if (silu_needs_exact(v[i], q[i])) {
+      if (m & (1u << i)) {
         // NaN can only arise here (every NaN or -inf input is flagged): make
         // it the canonical quiet NaN, so the rounding below needs no check
         const float e = silu_exact(v[i]);

@@ -422,6 +422,22 @@ gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen, co
   if (conv_state && !aligned(conv_state, 16)) return fail(GDN_ERR_INVALID_ARG, "conv_state must be 16-byte aligned");
   if (seqlen == 0 && (!cu_seqlens || !aligned(cu_seqlens, 4)))
     return fail(GDN_ERR_INVALID_ARG, "varlen (seqlen == 0) needs a 4-byte aligned cu_seqlens");
+  {
+    // the kernels read x and the window while they write y (and then the
+    // window from x): no two of them may share bytes
+    const size_t esz = dtype == GDN_BF16 ? 2 : 4;
+    auto overlap = [](const void* p, size_t pn, const void* q, size_t qn) {
+      const char* a0 = static_cast<const char*>(p);
+      const char* b0 = static_cast<const char*>(q);
+      return pn && qn && a0 < b0 + qn && b0 < a0 + pn;
+    };
+    const size_t xb = total_tokens > 0 ? ((size_t)(total_tokens - 1) * stride_x + channels) * esz : 0;
+    const size_t yb = total_tokens > 0 ? ((size_t)(total_tokens - 1) * stride_y + channels) * esz : 0;
+    const size_t wb = conv_state ? (size_t)num_seqs * (width - 1) * channels * esz : 0;
+    if (overlap(x, xb, y, yb)) return fail(GDN_ERR_INVALID_ARG, "x and y must not overlap");
+    if (overlap(conv_state, wb, x, xb) || overlap(conv_state, wb, y, yb))
+      return fail(GDN_ERR_INVALID_ARG, "conv_state must not overlap x or y");
+  }
   gdn::ConvArgs a;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;

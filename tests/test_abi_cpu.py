@@ -129,6 +129,12 @@ def test_entry_points_reject_before_any_gpu_call(g):
     assert L.gdn_conv1d(1, 10, 10, None, 64, 9, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 2   # width
     assert L.gdn_conv1d(1, 10, 10, None, 64, 4, 1, 18, 64, 16, None, None, 1, 16, 64, None) == 1   # x misaligned
     assert L.gdn_conv1d(1, 10, 0, None, 64, 4, 1, 16, 64, 16, None, None, 1, 16, 64, None) == 1    # varlen w/o cu
+    # x, y, conv_state must not share bytes (10 rows of 64 bf16 channels: 1280 bytes each)
+    X, Y, WIN = 1 << 26, 1 << 27, 1 << 28
+    assert L.gdn_conv1d(1, 10, 10, None, 64, 4, 1, X, 64, 16, None, None, 1, X + 1264, 64, None) == 1  # y in x
+    assert L.gdn_conv1d(1, 10, 10, None, 64, 4, 1, X, 64, 16, None, Y + 1024, 1, Y, 64, None) == 1     # window in y
+    assert L.gdn_conv1d(1, 10, 10, None, 64, 4, 1, X, 64, 16, None, X - 368, 1, Y, 64, None) == 1      # x in window
+    assert "overlap" in g.last_error()
     d = _dims(g)
     ws = g.workspace_size(d)
     args = [ctypes.byref(d), 16, 16, 16, 16, 16, None, None, 16, None]

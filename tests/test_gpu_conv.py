@@ -69,11 +69,15 @@ def test_conv_varlen_bitexact(G, orc, dtype, width):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_conv_dense_and_step(G, orc, dtype):
+@pytest.mark.parametrize("T", [33, 32])
+def test_conv_dense_and_step(G, orc, dtype, T):
+    """T = 32: every sequence starts on a 16-token span boundary, so each
+    span at a sequence start reads its halo from that sequence's window;
+    T = 33: sequence starts fall inside spans."""
     import torch
-    note(f"conv dense + decode step dtype={dtype}")
+    note(f"conv dense + decode step dtype={dtype} T={T}")
     r = np.random.default_rng(5)
-    B, T, C, W = 3, 33, 64, 4
+    B, C, W = 3, 64, 4
     x = r.normal(size=(B * T, C)).astype(np.float32)
     if dtype == "bf16":
         x = synth.round_bf16(x)
@@ -176,20 +180,24 @@ def test_silu_bf16_every_fp32_preactivation(G, orc):
     all taps zero the pre-activation is exactly the channel's fp32 bias
     (fma(0, 0, b) = b), so 1024 launches of 2^22 channels, each channel's
     bias one of the 2^32 bit patterns, give SiLU rounded to bf16 for every
-    fp32 value -- on the kernel's general path (first rows of the sequence)
-    and on its fast path (rows whose window lies inside the sequence).  Each
-    must equal the oracle's fp32 definition (Cody-Waite exponential, exact
-    division, round to nearest even) bit for bit; the test stops at the
+    fp32 value -- on each of the kernel's three walks over two 36-token
+    sequences: a full 32-token span from the first sequence's start (zero
+    halo, rows 0 and 20), the token-by-token walk of the span that the
+    second sequence starts inside (row 33) and the ragged last span
+    (row 70).  Each must equal the oracle's fp32 definition (Cody-Waite
+    exponential, exact division, round to nearest even) bit for bit; the
+    test stops at the
     first launch with a mismatch and names its input.  About 16 s on one
     MI355X with 16 host threads for the oracle."""
     import threading
 
     import torch
-    C, T, NBLK = 1 << 22, 32, 1 << 10
+    C, S, NSEQ, NBLK = 1 << 22, 36, 2, 1 << 10
+    T = S * NSEQ
+    rows = [0, 20, 33, 70]
     x = torch.zeros((T, C), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((C, 4), dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
-    conv = G.Conv1d(x, w, seqlen=T)
     x1 = np.zeros((1, C), dtype=np.float32)
     w1 = np.zeros((C, 4), dtype=np.float32)
     cu1 = np.array([0, 1], dtype=np.int32)
@@ -197,9 +205,9 @@ def test_silu_bf16_every_fp32_preactivation(G, orc):
     for blk in range(NBLK):
         a = (np.arange(C, dtype=np.uint64) + np.uint64(blk) * np.uint64(C)).astype(np.uint32).view(np.float32)
         bias = torch.from_numpy(a).cuda()
-        conv = G.Conv1d(x, w, seqlen=T, bias=bias)
+        conv = G.Conv1d(x, w, seqlen=S, num_seqs=NSEQ, bias=bias)
         conv(x, y)
-        got = _bits(y[[0, T // 2]])
+        got = _bits(y[rows])
         ref = np.empty(C, dtype=np.uint16)
 
         def part(i):
@@ -211,9 +219,9 @@ def test_silu_bf16_every_fp32_preactivation(G, orc):
             t.start()
         for t in th:
             t.join()
-        for row in (0, 1):
+        for row, path in enumerate(("full span, sequence start", "full span", "token-by-token", "ragged span")):
             bad = np.flatnonzero(got[row] != ref)
-            assert bad.size == 0, (f"block {blk}, row {'general' if row == 0 else 'fast'} path: {bad.size} "
+            assert bad.size == 0, (f"block {blk}, {path} path: {bad.size} "
                                    f"mismatches, first a bits {a.view(np.uint32)[bad[0]]:#010x}: "
                                    f"got {got[row][bad[0]]:#06x} want {ref[bad[0]]:#06x}")
         if blk % 64 == 0:
