@@ -264,7 +264,10 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
   const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
   // ---- load K and Q rows (zero past the end of the sequence) and the
-  // gates; all loads are issued before any is used
+  // gates; all loads are issued before any is used.  Rows and lanes outside
+  // the chunk read a clamped, valid address and are masked afterwards: a
+  // load inside a branch makes the compiler drain every load in flight
+  // where the branch rejoins (one more memory round trip each).
   constexpr int EPV = 16 / sizeof(T);
   constexpr int VPR = DK / EPV;  // 16-byte vectors per row
   constexpr int KQV = (WQ ? 2 : 1) * C * VPR;    // 16-byte vectors of K (and Q)
@@ -279,21 +282,24 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
       const int which = idx / (C * VPR);
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
-      w[j] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < KQV && r < len) {
-        const T* src = which ? qp + (long)(start + r) * a.stride_q : kp + (long)(start + r) * a.stride_k;
+      const int rr = min(r, len - 1);
+      if (KQV % PT == 0 || idx < KQV) {
+        const T* src = which ? qp + (long)(start + rr) * a.stride_q : kp + (long)(start + rr) * a.stride_k;
         w[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
+        if (r >= len) w[j] = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        w[j] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
   float gv = 0.f, bv = 0.f;
-  if (wave < HPW && lane < len) {
-    if (a.gate_a) {
-      gates_from_raw<E>(a, start + lane, hs[wave], gv, bv);
-    } else {
-      gv = a.g[(long)(start + lane) * a.hv + hs[wave]];
-      bv = a.beta[(long)(start + lane) * a.hv + hs[wave]];
-    }
+  if (a.gate_a) {
+    if (wave < HPW && lane < len) gates_from_raw<E>(a, start + lane, hs[wave], gv, bv);
+  } else {
+    const bool mine = wave < HPW && lane < len;
+    const long gi = (long)(start + min(lane, len - 1)) * a.hv + hs[wave < HPW ? wave : 0];
+    gv = mine ? a.g[gi] : 0.f;
+    bv = mine ? a.beta[gi] : 0.f;
   }
 
   // ---- stage K and Q into LDS with the per-row inverse norms

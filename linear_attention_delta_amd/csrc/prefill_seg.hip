@@ -508,22 +508,41 @@ __global__ void __launch_bounds__(64 * NW) k_seg_pass1(ScanArgs a) {
   f32x4 Z[NDT][NCT];
   const float* sin = (sg.p == 0 && a.state_in) ? a.state_in + ((long)sg.seq * a.hv + h) * DK * DV : nullptr;
   float* sst = a.seg_state + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DV;
+  // Z = [S | Phi]: S from state_in (first segment) or zero, Phi = I.  The
+  // state_in branch encloses its whole loop so that its loads all issue
+  // before the first wait.
 #pragma unroll
   for (int j = 0; j < NCT; j++) {
     const int gt = wave * NCT + j;
     vcol[j] = gt < SVT ? 16 * gt : -1;
     const int col = gt < SVT ? 16 * gt + c16 : 16 * (gt - SVT) + c16;
 #pragma unroll
-    for (int u = 0; u < NDT; u++) {
+    for (int u = 0; u < NDT; u++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int row = 16 * u + r4 + e;
-        if (gt < SVT) Z[u][j][e] = sin ? sin[(long)row * DV + col] : 0.f;
-        else Z[u][j][e] = row == col ? 1.f : 0.f;
+      for (int e = 0; e < 4; e++) Z[u][j][e] = (gt >= SVT && 16 * u + r4 + e == col) ? 1.f : 0.f;
+  }
+  if (sin) {
+#pragma unroll
+    for (int j = 0; j < NCT; j++) {
+      const int gt = wave * NCT + j;
+      if (gt < SVT) {
+#pragma unroll
+        for (int u = 0; u < NDT; u++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) Z[u][j][e] = sin[(long)(16 * u + r4 + e) * DV + 16 * gt + c16];
       }
-      // the first segment records its start state for pass 2 (the caller's
-      // state_in may be overwritten by state_out meanwhile)
-      if (sg.p == 0 && gt < SVT) *reinterpret_cast<f32x4*>(sst + state_frag<DV>(u, gt, lane)) = Z[u][j];
+    }
+  }
+  // the first segment records its start state for pass 2 (the caller's
+  // state_in may be overwritten by state_out meanwhile)
+  if (sg.p == 0) {
+#pragma unroll
+    for (int j = 0; j < NCT; j++) {
+      const int gt = wave * NCT + j;
+      if (gt < SVT) {
+#pragma unroll
+        for (int u = 0; u < NDT; u++) *reinterpret_cast<f32x4*>(sst + state_frag<DV>(u, gt, lane)) = Z[u][j];
+      }
     }
   }
 
@@ -784,17 +803,29 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   const float* sin = a.state_in ? a.state_in + ((long)sg.seq * a.hv + h) * DK * DV : nullptr;
   const float* sws = a.seg_state + ((long)(sg.sbase + sg.p) * a.hv + h) * DK * DV;
 #pragma unroll
-  for (int j = 0; j < NCT; j++) {
-    vcol[j] = 16 * (wave * NCT + j);
+  for (int j = 0; j < NCT; j++) vcol[j] = 16 * (wave * NCT + j);
+  // The start state: the branches enclose whole loops, so that each issues
+  // all its loads before the first wait (a branch around each load makes
+  // the compiler drain the loads in flight where it rejoins: one memory
+  // round trip per tile).
+  if (sg.nseg > 1) {
 #pragma unroll
-    for (int u = 0; u < NDT; u++) {
-      if (sg.nseg > 1) {
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int u = 0; u < NDT; u++)
         Z[u][j] = *reinterpret_cast<const f32x4*>(sws + state_frag<DV>(u, wave * NCT + j, lane));
-      } else {
+  } else if (sin) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) Z[u][j][e] = sin ? sin[(long)(16 * u + r4 + e) * DV + vcol[j] + c16] : 0.f;
-      }
-    }
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int u = 0; u < NDT; u++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) Z[u][j][e] = sin[(long)(16 * u + r4 + e) * DV + vcol[j] + c16];
+  } else {
+#pragma unroll
+    for (int j = 0; j < NCT; j++)
+#pragma unroll
+      for (int u = 0; u < NDT; u++) Z[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const long orow = (long)a.hv * DV;
   uint16_t* obase = reinterpret_cast<uint16_t*>(a.o) + (long)sg.s0 * orow + (long)h * DV;
