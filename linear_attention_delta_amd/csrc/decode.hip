@@ -145,27 +145,33 @@ __global__ void __launch_bounds__(256) k_decode(ScanArgs a) {
     return;
   }
   float* S = a.state + ((long)slot * a.hv + h) * (DK * DV);
-  f32x4 s[T::RPT];
-  load_state<DK, DV>(S, rg, cg, s);
 
   __shared__ float ks[DK], qs[DK];
   __shared__ float part[4][3];
   __shared__ f32x4 red[T::RG][T::CG][2];
 
+  // The token's q, k, v first, then the state stream: the load counter
+  // retires in order, so the q/k norms wait only for the loads before the
+  // stream and run while it arrives.  Every thread loads (threads past DK
+  // a clamped element, zeroed): a load inside a branch would make the
+  // compiler drain every load in flight where the branch rejoins.
   const int hk = a.tiled ? (h % a.hk) : (h / (a.hv / a.hk));
-  float kv_ = 0.f, qv_ = 0.f;
+  const int ti = tid < DK ? tid : tid % DK;
+  float kv_ = load_elem<E>(a.k, (long)b * a.stride_k + (long)hk * DK + ti);
+  float qv_ = load_elem<E>(a.q, (long)b * a.stride_q + (long)hk * DK + ti);
+  float vv[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) vv[j] = load_elem<E>(a.v, (long)b * a.stride_v + (long)h * DV + 4 * cg + j);
+  const float g = a.g[(long)b * a.hv + h];
+  const float beta = a.beta[(long)b * a.hv + h];
+  f32x4 s[T::RPT];
+  load_state<DK, DV>(S, rg, cg, s);
+  if (tid >= DK) kv_ = qv_ = 0.f;
   if (tid < DK) {
-    kv_ = load_elem<E>(a.k, (long)b * a.stride_k + (long)hk * DK + tid);
-    qv_ = load_elem<E>(a.q, (long)b * a.stride_q + (long)hk * DK + tid);
     ks[tid] = kv_;
     qs[tid] = qv_;
   }
   qk_partials(kv_, qv_, lane, wave, part);
-  const float g = a.g[(long)b * a.hv + h];
-  const float beta = a.beta[(long)b * a.hv + h];
-  float vv[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) vv[j] = load_elem<E>(a.v, (long)b * a.stride_v + (long)h * DV + 4 * cg + j);
   lds_barrier();
   head_step<E, DK, DV>(s, ks, qs, vv, g, beta, qk_factors(part, a.l2norm, a.scale), red, rg, cg, op, S);
 }

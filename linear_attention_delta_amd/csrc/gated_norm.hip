@@ -70,6 +70,12 @@ __global__ void __launch_bounds__(256) k_gated_norm(NormArgs a) {
   typedef typename E::store_t T;
   const int part = threadIdx.x % LPR;
   const long row0 = (long)blockIdx.x * (RPB * R) + threadIdx.x / LPR;
+  // All loads are issued before any is used and none sits in a branch (the
+  // compiler drains every load in flight where a branch around one
+  // rejoins): rows past the end read the last row and are zeroed.
+  float w[V];
+#pragma unroll
+  for (int i = 0; i < V; i++) w[i] = a.weight[part * V + i];
   float o[R][V], z[R][V];
   long t[R];
   int h[R];
@@ -78,21 +84,31 @@ __global__ void __launch_bounds__(256) k_gated_norm(NormArgs a) {
     const long row = row0 + k * RPB;
     // every lane of a row stays through the shuffles below; rows past the
     // end contribute zeros and store nothing
-    const bool live = row < a.rows;
-    t[k] = live ? row / a.heads : 0;
-    h[k] = live ? (int)(row % a.heads) : 0;
-    const long col = (long)h[k] * DV + part * V;
-    if (live) {
-      Word<E>::load(reinterpret_cast<const T*>(a.o) + t[k] * a.stride_o + col, o[k]);
-      Word<E>::load(reinterpret_cast<const T*>(a.z) + t[k] * a.stride_z + col, z[k]);
+    const long rr = row < a.rows ? row : a.rows - 1;
+    if (a.rows <= 0xffffffffL) {  // 32-bit division where it suffices
+      const uint32_t r32 = (uint32_t)rr, tq = r32 / (uint32_t)a.heads;
+      t[k] = tq;
+      h[k] = (int)(r32 - tq * (uint32_t)a.heads);
     } else {
+      t[k] = rr / a.heads;
+      h[k] = (int)(rr - t[k] * a.heads);
+    }
+    const long col = (long)h[k] * DV + part * V;
+    Word<E>::load(reinterpret_cast<const T*>(a.o) + t[k] * a.stride_o + col, o[k]);
+    Word<E>::load(reinterpret_cast<const T*>(a.z) + t[k] * a.stride_z + col, z[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < R; k++) {
+    // z is used only by the store below; this empty statement takes it as
+    // an input so that the compiler cannot sink its load past the row
+    // reduction (it would then be a second round trip after the first)
+#pragma unroll
+    for (int i = 0; i < V; i++) asm volatile("" ::"v"(z[k][i]));
+    if (row0 + k * RPB >= a.rows) {
 #pragma unroll
       for (int i = 0; i < V; i++) o[k][i] = z[k][i] = 0.0f;
     }
   }
-  float w[V];
-#pragma unroll
-  for (int i = 0; i < V; i++) w[i] = a.weight[part * V + i];
 #pragma unroll
   for (int k = 0; k < R; k++) {
     float ss = 0.0f;
