@@ -755,6 +755,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
   static_assert(NCT * 16 * NCW == DV, "state columns must split over the carry waves");
   __shared__ SM sm;
   __shared__ float nss[NORM ? 2 * NCW * C : 1];  // [parity][carry wave][token]: row sums of o^2
+  __shared__ __align__(16) float nwl[NORM ? DV : 4];  // the norm weight, read by the carry waves from LDS
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c16 = lane & 15, r4 = 4 * (lane >> 4);
   int n, hk, h;
@@ -863,14 +864,12 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
       store_rows(i, ob);
     }
   } else {
-    // the fused gated norm (see above); the previous chunk's o in obp, the
-    // weights of this lane's columns in wn
+    // the fused gated norm (see above); the previous chunk's o in obp.  The
+    // weights are read from LDS where they are used: held in registers
+    // across the carry they made the kernel spill, and every spill reload
+    // waited for all the o stores in flight (one load counter, in order).
     u32x2 obp[NCT][C / 16];
-    float wn[NCT][4];
-#pragma unroll
-    for (int j = 0; j < NCT; j++)
-#pragma unroll
-      for (int e = 0; e < 4; e++) wn[j][e] = a.norm_w[vcol[j] + r4 + e];
+    for (int c = tid; c < DV; c += 64 * NCW) nwl[c] = a.norm_w[c];  // published by the loop's first barrier
     // this wave's part of each row's sum of squares -> LDS slot of the parity
     auto row_sums = [&](int i) {
 #pragma unroll
@@ -890,6 +889,9 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
     // y of chunk i from obp, the published row sums and the gate rows the
     // staging waves left in the chunk's V buffer; y overwrites obp
     auto finish = [&](int i) {
+      f32x4 wn[NCT];
+#pragma unroll
+      for (int j = 0; j < NCT; j++) wn[j] = *reinterpret_cast<const f32x4*>(&nwl[vcol[j] + r4]);
 #pragma unroll
       for (int t = 0; t < C / 16; t++) {
         float ss = 0.f;
