@@ -59,22 +59,36 @@ __device__ __forceinline__ float silu_fast(float a) {
 }
 
 // Eight SiLU outputs of a 16-byte bf16 word, each equal to silu<BF16> of its
-// input: the fast form for all eight, then one (rarely taken) branch that
-// redoes the flagged ones exactly, instead of a branch per element.
+// input: the fast form for all eight, then one branch that redoes the
+// flagged ones exactly.  The test for the branch is done for the word as a
+// whole, with few vector instructions (the kernel is bound by them): the
+// a > -8 compares combine as lane masks on the scalar unit, and the
+// distances of the eight results' low halves to the midpoint pattern are
+// formed two at a time in 16-bit lanes and reduced to their minimum.  Only
+// a taken branch (any of 64 lanes asking) tests the elements one by one.
+typedef unsigned short conv_u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void silu8_for_bf16(float (&v)[8]) {
-  // m: which of the eight need the exact form, kept as bits so that the
-  // (often taken: any of 64 lanes may ask) branch does not test them again
   float q[8];
-  uint32_t m = 0;
+  bool neg = false;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     q[i] = silu_fast(v[i]);
-    m |= silu_needs_exact(v[i], q[i]) ? 1u << i : 0u;
+    neg |= !(v[i] > -8.0f);
   }
-  if (m) {
+  conv_u16x2 d[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    // low 16 bits of q[2k] and q[2k+1] side by side, less (0x8000 - 16)
+    const uint32_t w = __builtin_amdgcn_perm(__float_as_uint(q[2 * k + 1]), __float_as_uint(q[2 * k]), 0x05040100u);
+    d[k] = __builtin_bit_cast(conv_u16x2, w) - conv_u16x2{0x8000 - 16, 0x8000 - 16};
+  }
+  const conv_u16x2 m01 = __builtin_elementwise_min(d[0], d[1]), m23 = __builtin_elementwise_min(d[2], d[3]);
+  const conv_u16x2 m = __builtin_elementwise_min(m01, m23);
+  const bool band = (m.x < m.y ? m.x : m.y) <= 32;
+  if (neg || band) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      if (m & (1u << i)) {
+      if (silu_needs_exact(v[i], q[i])) {
         // NaN can only arise here (every NaN or -inf input is flagged): make
         // it the canonical quiet NaN, so the rounding below needs no check
         const float e = silu_exact(v[i]);
