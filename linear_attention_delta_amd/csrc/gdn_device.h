@@ -109,17 +109,31 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const typename E::store_t* 
 
 // ---------------------------------------------------------- reductions
 
+// v plus the value of the lane 16 (or 32) apart, in every lane, through the
+// row swaps v_permlane16_swap / v_permlane32_swap (odd 16- or 32-lane rows of
+// the first operand traded with even rows of the second), with no trip
+// through the LDS.  Each lane adds its own value and its partner's; the sum
+// is the same either way round.
+__device__ __forceinline__ float add_lane_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32 or 64), every lane
 // of a group receiving the group's sum.  Within 16-lane rows the exchange
-// uses DPP lane swizzles (no LDS traffic).
+// uses DPP lane swizzles, across rows the row swaps (no LDS traffic).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if (N >= 2) v += __builtin_amdgcn_update_dpp(0.f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
   if (N >= 4) v += __builtin_amdgcn_update_dpp(0.f, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
   if (N >= 8) v += __builtin_amdgcn_update_dpp(0.f, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
   if (N >= 16) v += __builtin_amdgcn_update_dpp(0.f, v, 0x140, 0xF, 0xF, false); // row_mirror
-  if (N >= 32) v += __shfl_xor(v, 16, 64);
-  if (N >= 64) v += __shfl_xor(v, 32, 64);
+  if (N >= 32) v = add_lane_xor16(v);
+  if (N >= 64) v = add_lane_xor32(v);
   return v;
 }
 

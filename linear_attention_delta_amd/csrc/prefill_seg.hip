@@ -842,12 +842,14 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
       const int tok = 16 * t + c16;
       if constexpr (NCT == 2) {
         // lanes g and g^1 (16 apart) trade halves so that each writes 8
-        // adjacent columns: even g the first tile, odd g the second
+        // adjacent columns: even g the first tile, odd g the second.  The
+        // row swap (odd 16-lane rows of the first operand with even rows of
+        // the second) leaves every lane exactly its 8 columns, in order,
+        // with no trip through the LDS.
         const bool ev = ((lane >> 4) & 1) == 0;
-        const u32x2 send = ev ? rows[1][t] : rows[0][t];
-        const u32x2 recv = {(uint32_t)__shfl_xor((int)send[0], 16, 64), (uint32_t)__shfl_xor((int)send[1], 16, 64)};
-        const u32x4 w = ev ? u32x4{rows[0][t][0], rows[0][t][1], recv[0], recv[1]}
-                           : u32x4{recv[0], recv[1], rows[1][t][0], rows[1][t][1]};
+        const auto s0 = __builtin_amdgcn_permlane16_swap(rows[0][t][0], rows[1][t][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(rows[0][t][1], rows[1][t][1], false, false);
+        const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
         const int col = ev ? vcol[0] + r4 : vcol[1] + r4 - 4;
         if (tok < clen) *reinterpret_cast<u32x4*>(oc + (long)tok * orow + col) = w;
       } else if (tok < clen) {
@@ -881,8 +883,7 @@ __global__ void __launch_bounds__(64 * (NCW + 4)) k_seg_pass2(ScanArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; e++) ss += o4[e] * o4[e];
         }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
+        ss = add_lane_xor32(add_lane_xor16(ss));
         if (lane < 16) nss[((i & 1) * NCW + wave) * C + 16 * t + c16] = ss;
       }
     };
