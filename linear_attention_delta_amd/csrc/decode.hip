@@ -219,16 +219,27 @@ struct ConvChannel {
     raw[W - 1] = xr[ch];
 #pragma unroll
     for (int j = 0; j < W; j++) wj[j] = weight[ch * W + j];
-    bias = bias_ ? bias_[ch] : 0.0f;
+    // no load in a branch (the compiler would drain every load in flight
+    // where it rejoins): a missing bias reads a tap and is masked to +0
+    const float bl = (bias_ ? bias_ : weight)[ch];
+    bias = __uint_as_float(__float_as_uint(bl) & (bias_ ? ~0u : 0u));
   }
-  __device__ __forceinline__ float finish() {
+  // the output as the stand-alone convolution stores it
+  __device__ __forceinline__ float value() const {
     float xv[W];
 #pragma unroll
     for (int j = 0; j < W; j++) xv[j] = E::to_f32(raw[j]);
-    const float y = conv_point<E, W, true>(bias, wj, xv);
+    return as_stored<E>(conv_point<E, W, true>(bias, wj, xv));
+  }
+  // the window advanced by the token (by the channel's owner only)
+  __device__ __forceinline__ void write_window() const {
 #pragma unroll
     for (int j = 0; j < W - 1; j++) win[j * cc + ch] = window_entry<E>(raw[j + 1]);
-    return as_stored<E>(y);
+  }
+  __device__ __forceinline__ float finish() {
+    const float y = value();
+    write_window();
+    return y;
   }
 };
 
@@ -240,7 +251,7 @@ struct ConvChannel {
 // its own head's v.  Every value that reaches the recurrence is the one the
 // stand-alone convolution would have stored, so the result equals the two
 // separate calls bit for bit.
-template <class E, int DK, int DV, int W>
+template <class E, int DK, int DV, int W, bool GATED>
 __global__ void __launch_bounds__(1024) k_decode_conv(ScanArgs a, ConvArgs c) {
   typedef Team<DK, DV> T;
   typedef typename E::store_t ST;
@@ -278,14 +289,19 @@ __global__ void __launch_bounds__(1024) k_decode_conv(ScanArgs a, ConvArgs c) {
   const long chq = hk * DK + tid, chk = (a.hk + hk) * DK + tid, chv = 2 * a.hk * DK + h * DV + tid;
   ConvChannel<E, W> cq, ck, cv;
   if constexpr (kEarly) {
-    if (qk) {
-      cq.load(xr, win, cc, c.weight, c.bias, chq);
-      ck.load(xr, win, cc, c.weight, c.bias, chk);
-    }
-    if (tid < DV) cv.load(xr, win, cc, c.weight, c.bias, chv);
+    // every thread loads (threads that own no channel a clamped one, whose
+    // value is computed and dropped): loads inside the ownership branches
+    // were drained where those rejoined, one round trip before the state
+    // stream went out
+    const int tq = tid % DK, tv = tid % DV;
+    cq.load(xr, win, cc, c.weight, c.bias, hk * DK + tq);
+    ck.load(xr, win, cc, c.weight, c.bias, (a.hk + hk) * DK + tq);
+    cv.load(xr, win, cc, c.weight, c.bias, 2 * a.hk * DK + h * DV + tv);
   }
+  // the gates: two instantiations rather than a branch, whose loads the
+  // compiler drained before the state stream went out
   float g, beta;
-  if (a.gate_a) {
+  if constexpr (GATED) {
     gates_from_raw<E>(a, b, h, g, beta);
   } else {
     g = a.g[(long)b * a.hv + h];
@@ -293,22 +309,42 @@ __global__ void __launch_bounds__(1024) k_decode_conv(ScanArgs a, ConvArgs c) {
   }
   if constexpr (kEarly) load_state<DK, DV>(S, rg, cg, s);
 
-  // late loads go one channel at a time, to keep fewer values live
-  if (team == 0) {
-    float kv_ = 0.f, qv_ = 0.f;
-    if (qk) {
-      if constexpr (!kEarly) cq.load(xr, win, cc, c.weight, c.bias, chq);
-      qv_ = cq.finish();
-      if constexpr (!kEarly) ck.load(xr, win, cc, c.weight, c.bias, chk);
-      kv_ = ck.finish();
-      ks[tid] = kv_;
-      qs[tid] = qv_;
+  if constexpr (kEarly) {
+    // the values for every thread, unconditionally, so that the loads above
+    // stay ahead of the state stream; only the owners keep them
+    const float qv0 = cq.value(), kv0 = ck.value(), vv0 = cv.value();
+    if (team == 0) {
+      const float kv_ = qk ? kv0 : 0.f, qv_ = qk ? qv0 : 0.f;
+      if (qk) {
+        cq.write_window();
+        ck.write_window();
+        ks[tid] = kv_;
+        qs[tid] = qv_;
+      }
+      qk_partials(kv_, qv_, lane, wave, part);
     }
-    qk_partials(kv_, qv_, lane, wave, part);
-  }
-  if (tid < DV) {
-    if constexpr (!kEarly) cv.load(xr, win, cc, c.weight, c.bias, chv);
-    vs[team][tid] = cv.finish();
+    if (tid < DV) {
+      cv.write_window();
+      vs[team][tid] = vv0;
+    }
+  } else {
+    // late loads go one channel at a time, to keep fewer values live
+    if (team == 0) {
+      float kv_ = 0.f, qv_ = 0.f;
+      if (qk) {
+        cq.load(xr, win, cc, c.weight, c.bias, chq);
+        qv_ = cq.finish();
+        ck.load(xr, win, cc, c.weight, c.bias, chk);
+        kv_ = ck.finish();
+        ks[tid] = kv_;
+        qs[tid] = qv_;
+      }
+      qk_partials(kv_, qv_, lane, wave, part);
+    }
+    if (tid < DV) {
+      cv.load(xr, win, cc, c.weight, c.bias, chv);
+      vs[team][tid] = cv.finish();
+    }
   }
   lds_barrier();
   float vv[4];
@@ -334,16 +370,23 @@ hipError_t launch_conv_dims(const ScanArgs& a, const ConvArgs& c, hipStream_t st
   const int group = a.hv / a.hk;
   if (group > 4) return hipErrorInvalidValue;
   dim3 grid(a.hk * a.num_seqs), block(256 * group);
+  const bool gated = a.gate_a != nullptr;
+#define GDN_DECODE_CONV_W(WW)                                                                   \
+  case WW:                                                                                     \
+    if (gated) hipLaunchKernelGGL((k_decode_conv<E, DK, DV, WW, true>), grid, block, 0, st, a, c); \
+    else hipLaunchKernelGGL((k_decode_conv<E, DK, DV, WW, false>), grid, block, 0, st, a, c);      \
+    break;
   switch (c.width) {
-    case 2: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 2>), grid, block, 0, st, a, c); break;
-    case 3: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 3>), grid, block, 0, st, a, c); break;
-    case 4: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 4>), grid, block, 0, st, a, c); break;
-    case 5: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 5>), grid, block, 0, st, a, c); break;
-    case 6: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 6>), grid, block, 0, st, a, c); break;
-    case 7: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 7>), grid, block, 0, st, a, c); break;
-    case 8: hipLaunchKernelGGL((k_decode_conv<E, DK, DV, 8>), grid, block, 0, st, a, c); break;
+    GDN_DECODE_CONV_W(2)
+    GDN_DECODE_CONV_W(3)
+    GDN_DECODE_CONV_W(4)
+    GDN_DECODE_CONV_W(5)
+    GDN_DECODE_CONV_W(6)
+    GDN_DECODE_CONV_W(7)
+    GDN_DECODE_CONV_W(8)
     default: return hipErrorInvalidValue;
   }
+#undef GDN_DECODE_CONV_W
   return hipGetLastError();
 }
 
