@@ -326,29 +326,40 @@ __global__ void __launch_bounds__(256) k_conv_step(ConvArgs a) {
   const T* x = reinterpret_cast<const T*>(a.x);
   T* y = reinterpret_cast<T*>(a.y);
   T* win = reinterpret_cast<T*>(a.conv_state);
-  float hist[W][V];
-  if (win) {
+  // Every load is issued before any value is used, with no load under a
+  // branch: a missing window reads this token's row in its place and a
+  // missing bias reads the weights, both masked to zero afterwards.
+  const bool has_win = win != nullptr, has_bias = a.bias != nullptr;
+  const T* xrow = x + (long)seq * a.stride_x + c0;
+  typename Vec<E>::raw_t raw[W];
 #pragma unroll
-    for (int j = 0; j < W - 1; j++)
-      Vec<E>::load(win + ((long)seq * (W - 1) + j) * a.channels + c0, hist[j]);
-  } else {
+  for (int j = 0; j < W - 1; j++)
+    raw[j] = Vec<E>::load_raw(has_win ? win + ((long)seq * (W - 1) + j) * a.channels + c0 : xrow);
+  raw[W - 1] = Vec<E>::load_raw(xrow);
+  const float* bsrc = has_bias ? a.bias : a.weight;
+  float bias[V], wj[V][W];
 #pragma unroll
-    for (int j = 0; j < W - 1; j++)
+  for (int i = 0; i < V; i++) {
+    bias[i] = bsrc[c0 + i];
 #pragma unroll
-      for (int i = 0; i < V; i++) hist[j][i] = 0.0f;
+    for (int j = 0; j < W; j++) wj[i][j] = a.weight[(long)(c0 + i) * W + j];
   }
-  Vec<E>::load(x + (long)seq * a.stride_x + c0, hist[W - 1]);
+  float hist[W][V];
+#pragma unroll
+  for (int j = 0; j < W; j++) {
+    Vec<E>::cvt(raw[j], hist[j]);
+    if (j < W - 1)
+#pragma unroll
+      for (int i = 0; i < V; i++) hist[j][i] = has_win ? hist[j][i] : 0.0f;
+  }
   float out[V];
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    const float bias = a.bias ? a.bias[c0 + i] : 0.0f;
-    float wj[W], xv[W];
+    float xv[W];
 #pragma unroll
-    for (int j = 0; j < W; j++) {
-      wj[j] = a.weight[(long)(c0 + i) * W + j];
-      xv[j] = hist[j][i];
-    }
-    out[i] = a.activation ? conv_point<E, W, true>(bias, wj, xv) : conv_point<E, W, false>(bias, wj, xv);
+    for (int j = 0; j < W; j++) xv[j] = hist[j][i];
+    const float b = has_bias ? bias[i] : 0.0f;
+    out[i] = a.activation ? conv_point<E, W, true>(b, wj[i], xv) : conv_point<E, W, false>(b, wj[i], xv);
   }
   Vec<E>::store(y + (long)seq * a.stride_y + c0, out);
   if (win) {
