@@ -94,9 +94,39 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 // D += A[row0.., k0..k0+K) * B[k0..k0+K), col0..) where A is row-major with
 // leading dimension lda and B is given TRANSPOSED (BT row-major [col][k],
 // leading dimension ldb) -- both operands then read KPL contiguous elements.
-template <class E, int K>
+// fp32 operands (K a multiple of 16): the 16 k of four consecutive 16x16x4
+// steps are regrouped so that each lane's four values sit side by side
+// (step i, lane (r, q) takes k = kb + 4q + i), so each operand is one
+// 16-byte read per four steps instead of one 4-byte read per step.  Every k
+// is used exactly once, by the same lane of A and B.  Rows of A and BT must
+// be 16-byte aligned.  BATCH: every read in flight before the first product
+// (left to itself, the compiler waits on each pair right after issuing it;
+// batching costs 8 VGPRs per 16 k).
+template <int K, bool BATCH>
+__device__ __forceinline__ f32x4 tile_mma_f32(f32x4 acc, const float* A, int lda, const float* BT, int ldb,
+                                              int lane) {
+  static_assert(K % 16 == 0, "K must be a multiple of 16");
+  const int r = lane & 15, kq = (lane >> 4) * 4;
+  const float* pa = A + r * lda + kq;
+  const float* pb = BT + r * ldb + kq;
+  f32x4 a4[K / 16], b4[K / 16];
+#pragma unroll
+  for (int j = 0; j < K / 16; j++) {
+    a4[j] = *reinterpret_cast<const f32x4*>(pa + 16 * j);
+    b4[j] = *reinterpret_cast<const f32x4*>(pb + 16 * j);
+  }
+  if constexpr (BATCH) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < K / 16; j++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc = mfma16(a4[j][i], b4[j][i], acc);
+  return acc;
+}
+
+template <class E, int K, bool BATCH = false>
 __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const typename E::store_t* A, int lda,
                                           const typename E::store_t* BT, int ldb, int lane) {
+  if constexpr (E::KSTEP == 4 && K % 16 == 0) return tile_mma_f32<K, BATCH>(acc, A, lda, BT, ldb, lane);
   const int r = lane & 15, kq = (lane >> 4) * E::KPL;
   const typename E::store_t* pa = A + r * lda + kq;
   const typename E::store_t* pb = BT + r * ldb + kq;

@@ -577,13 +577,21 @@ struct alignas(16) ScanSmem {
   T u2t[NT][16][CLD];          // (diag(c) U)^T
 };
 
-// D += A B where A(16 x K) = M^T for M row-major [K][ld] (fp32 operands).
+// D += A B where A(16 x K) = M^T for M row-major [K][ld] (fp32 operands,
+// K a multiple of 16).  The k of four consecutive steps are regrouped as in
+// tile_mma_f32 (step i, lane (r, q): k = kb + 4q + i), so B is one 16-byte
+// read per four steps; A is a column of M, four 4-byte reads.
 template <int K>
 __device__ __forceinline__ f32x4 tile_mma_at_f32(f32x4 acc, const float* M, int ldm, const float* BT, int ldb,
                                                  int lane) {
-  const int r = lane & 15, q = lane >> 4;
+  static_assert(K % 16 == 0, "K must be a multiple of 16");
+  const int r = lane & 15, kq = (lane >> 4) * 4;
 #pragma unroll
-  for (int kb = 0; kb < K; kb += 4) acc = mfma16(M[(kb + q) * ldm + r], BT[r * ldb + kb + q], acc);
+  for (int kb = 0; kb < K; kb += 16) {
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(BT + r * ldb + kb + kq);
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc = mfma16(M[(kb + kq + i) * ldm + r], b4[i], acc);
+  }
   return acc;
 }
 
@@ -609,9 +617,30 @@ __device__ __forceinline__ f32x4 tile_mma_kt_bf16(f32x4 acc, const uint16_t* K, 
   return acc;
 }
 
-template <class E>
+// D += A B over k < kend (kend a multiple of the MFMA K step, at most KMAX;
+// for fp32 a multiple of 16: the steps take the regrouped 16-byte reads of
+// tile_mma_f32, all KMAX of them issued first, the products then run for
+// the blocks below kend).
+template <class E, int KMAX>
 __device__ __forceinline__ f32x4 tile_mma_rt(f32x4 acc, const typename E::store_t* A, int lda,
                                              const typename E::store_t* BT, int ldb, int lane, int kend) {
+  if constexpr (E::KSTEP == 4 && KMAX % 16 == 0) {
+    const int r = lane & 15, kq = (lane >> 4) * 4;
+    f32x4 a4[KMAX / 16], b4[KMAX / 16];
+#pragma unroll
+    for (int j = 0; j < KMAX / 16; j++) {
+      a4[j] = *reinterpret_cast<const f32x4*>(A + r * lda + kq + 16 * j);
+      b4[j] = *reinterpret_cast<const f32x4*>(BT + r * ldb + kq + 16 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX / 16; j++) {
+      if (16 * j < kend) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc = mfma16(a4[j][i], b4[j][i], acc);
+      }
+    }
+    return acc;
+  }
   const int r = lane & 15, kq = (lane >> 4) * E::KPL;
   for (int kb = 0; kb < kend; kb += E::KSTEP)
     acc = mfma16(load_frag(A + r * lda + kq + kb, E()), load_frag(BT + r * ldb + kq + kb, E()), acc);
@@ -786,7 +815,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     // ---- X = K S, R = V - diag(a) X -> R^T
     if (lw < NRT) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      X = tile_mma<E, DK>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
+      X = tile_mma<E, DK, true>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
       const int s = 16 * lw + r4;
       st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
@@ -795,7 +824,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     if (lw < NRT) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 U = {0.f, 0.f, 0.f, 0.f};
-      U = tile_mma_rt<E>(U, &sm.tt[b][16 * lw][0], CLD, &sm.rt[tw][0][0], CLD, lane, kend);
+      U = tile_mma_rt<E, C>(U, &sm.tt[b][16 * lw][0], CLD, &sm.rt[tw][0][0], CLD, lane, kend);
       const int s = 16 * lw + r4;
       st4(&sm.ut[tw][c16][s], U);
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
@@ -804,10 +833,10 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT) {
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      Y = tile_mma<E, DK>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
+      Y = tile_mma<E, DK, true>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 PU = {0.f, 0.f, 0.f, 0.f};
-      PU = tile_mma_rt<E>(PU, &sm.ut[tw][0][0], CLD, &sm.p[b][16 * lw][0], CLD, lane, kend);
+      PU = tile_mma_rt<E, C>(PU, &sm.ut[tw][0][0], CLD, &sm.p[b][16 * lw][0], CLD, lane, kend);
       const int r = 16 * lw + c16;
       if (r < clen) st4(obase + (long)(cs + r) * a.hv * a.dv, sm.sc[b][1][r] * Y + PU);
     }
