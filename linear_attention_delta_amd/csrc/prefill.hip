@@ -708,15 +708,22 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   // ---- initial state: wave (tw, lw) owns rows [lw*DK/4, (lw+1)*DK/4) of tile tw
   f32x4 S[STW];
   {
+    // the branch encloses the whole loop, so that its loads all issue before
+    // the first wait (a branch around each load makes the compiler wait for
+    // the loads in flight where it rejoins: one memory round trip each)
     const float* sin = a.state_in ? a.state_in + ((long)seq * a.hv + h) * DK * a.dv : nullptr;
     const int col = dv0 + 16 * tw + c16;
+    if (sin) {
 #pragma unroll
-    for (int t = 0; t < STW; t++) {
-      const int rb = (lw * STW + t) * 16;
+      for (int t = 0; t < STW; t++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) S[t][e] = sin ? sin[(long)(rb + r4 + e) * a.dv + col] : 0.f;
-      st4(&sm.st[0][tw][c16][rb + r4], S[t]);
+        for (int e = 0; e < 4; e++) S[t][e] = sin[(long)((lw * STW + t) * 16 + r4 + e) * a.dv + col];
+    } else {
+#pragma unroll
+      for (int t = 0; t < STW; t++) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int t = 0; t < STW; t++) st4(&sm.st[0][tw][c16][(lw * STW + t) * 16 + r4], S[t]);
   }
 
   // ---- staging: all global loads of a chunk are issued at once into
@@ -738,39 +745,85 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   const T* mp = reinterpret_cast<const T*>(a.tinv);
   const float* scp = a.scal;
   u32x4 pkq[NKQ], pm[NM], pv = {0u, 0u, 0u, 0u}, ps = {0u, 0u, 0u, 0u};
+  // Each thread's element offsets, computed once: a chunk's load is its base
+  // plus the offset, with no 64-bit row-times-stride product per vector.
+  // Every load is unconditional (a load inside a branch makes the compiler
+  // wait for the loads in flight where the branch rejoins): a row past the
+  // sequence's end reads the chunk's first row and is zeroed at the store.
+  long kqo[NKQ], vo = 0;
+  int kq0[NKQ], kqr[NKQ], v0 = 0, vr = C;
+#pragma unroll
+  for (int j = 0; j < NKQ; j++) {
+    const int idx = tid + NTH * j;
+    const int which = idx / (C * VPR);
+    const int rem = idx % (C * VPR);
+    const int r = rem / VPR, cv = rem % VPR;
+    kqr[j] = idx < KQ_V ? r : C;
+    kq0[j] = hk * DK + cv * EPV;
+    kqo[j] = (long)r * (which ? a.stride_q : a.stride_k) + kq0[j];
+  }
+  if (tid < V_V) {
+    const int r = tid / V_VPR, cv = tid % V_VPR;
+    vr = r;
+    v0 = h * a.dv + dv0 + cv * EPV;
+    vo = (long)r * a.stride_v + v0;
+  }
+  int staged_len = C;  // valid rows of the chunk held in the registers
 
   auto load_chunk = [&](int ch) {
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
-#pragma unroll
-    for (int j = 0; j < NKQ; j++) {
-      const int idx = tid + NTH * j;
-      const int which = idx / (C * VPR);  // 0: K, 1: Q
-      const int rem = idx % (C * VPR);
-      const int r = rem / VPR, cv = rem % VPR;
-      pkq[j] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < KQ_V && r < clen) {
-        const T* src = which ? qp + (long)(cs + r) * a.stride_q : kp + (long)(cs + r) * a.stride_k;
-        pkq[j] = *reinterpret_cast<const u32x4*>(src + (long)hk * DK + cv * EPV);
-      }
-    }
+    staged_len = clen;
+    // in the order the stores below consume them (the load counter retires
+    // in order): V, then Tt and P, then K and Q, then the scalars
+    pv = *reinterpret_cast<const u32x4*>(vp + (long)cs * a.stride_v + (vr < clen ? vo : (long)v0));
     const long blk = (long)(cbase + ch) * a.hv + h;
     const T* msrc = mp + blk * (2 * C * C);
 #pragma unroll
-    for (int j = 0; j < NM; j++) {
+    for (int j = 0; j < NM; j++) pm[j] = *reinterpret_cast<const u32x4*>(msrc + min(tid + NTH * j, M_V - 1) * EPV);
+    const T* kc = kp + (long)cs * a.stride_k;
+    const T* qc = qp + (long)cs * a.stride_q;
+#pragma unroll
+    for (int j = 0; j < NKQ; j++) {
       const int idx = tid + NTH * j;
-      if (idx < M_V) pm[j] = *reinterpret_cast<const u32x4*>(msrc + idx * EPV);
+      const int which = idx / (C * VPR);
+      const T* src = (which ? qc : kc) + (kqr[j] < clen ? kqo[j] : (long)kq0[j]);
+      pkq[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+    ps = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
+  };
+
+  // The next chunk's staging goes in three parts, each as soon as no wave
+  // reads that array of the current chunk any more (in a single buffer):
+  // V^T once every wave is past R (after B1), Tt once every wave is past U
+  // (after B2), and the rest at the end of the chunk.
+  auto store_v = [&](int b) {
+    if (staged_len < C) {
+      // the sequence's last, partial chunk: rows past its end are zero (a
+      // branch with no memory access, taken by every lane or none)
+#pragma unroll
+      for (int j = 0; j < NKQ; j++)
+        if (kqr[j] >= staged_len) pkq[j] = u32x4{0u, 0u, 0u, 0u};
+      if (vr >= staged_len) pv = u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < V_V) {
       const int r = tid / V_VPR, cv = tid % V_VPR;
-      pv = u32x4{0u, 0u, 0u, 0u};
-      if (r < clen)
-        pv = *reinterpret_cast<const u32x4*>(vp + (long)(cs + r) * a.stride_v + (long)h * a.dv + dv0 + cv * EPV);
+      const T* e = reinterpret_cast<const T*>(&pv);
+#pragma unroll
+      for (int i = 0; i < EPV; i++) sm.vt[b][cv * EPV + i][r] = E::to_f32(e[i]);
     }
-    if (tid < S_V) ps = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + tid * 4);
   };
-
-  auto store_chunk = [&](int b) {
+  auto store_tt = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < NM; j++) {
+      const int idx = tid + NTH * j;
+      if (idx < C * C / EPV) {
+        const int r = idx / (C / EPV), cv = idx % (C / EPV);
+        *reinterpret_cast<u32x4*>(&sm.tt[b][r][cv * EPV]) = pm[j];
+      }
+    }
+  };
+  auto store_rest = [&](int b) {
 #pragma unroll
     for (int j = 0; j < NKQ; j++) {
       const int idx = tid + NTH * j;
@@ -782,25 +835,20 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
 #pragma unroll
     for (int j = 0; j < NM; j++) {
       const int idx = tid + NTH * j;
-      if (idx < M_V) {
-        const int which = idx / (C * C / EPV);
-        const int rem = idx % (C * C / EPV);
+      if (idx >= C * C / EPV && idx < M_V) {
+        const int rem = idx - C * C / EPV;
         const int r = rem / (C / EPV), cv = rem % (C / EPV);
-        *reinterpret_cast<u32x4*>(which ? &sm.p[b][r][cv * EPV] : &sm.tt[b][r][cv * EPV]) = pm[j];
+        *reinterpret_cast<u32x4*>(&sm.p[b][r][cv * EPV]) = pm[j];
       }
-    }
-    if (tid < V_V) {
-      const int r = tid / V_VPR, cv = tid % V_VPR;
-      const T* e = reinterpret_cast<const T*>(&pv);
-#pragma unroll
-      for (int i = 0; i < EPV; i++) sm.vt[b][cv * EPV + i][r] = E::to_f32(e[i]);
     }
     if (tid < S_V) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + tid * 4) = ps;
   };
 
   if (nchunks > 0) {
     load_chunk(0);
-    store_chunk(0);
+    store_v(0);
+    store_tt(0);
+    store_rest(0);
   }
   T* obase = reinterpret_cast<T*>(a.o) + (long)h * a.dv + dv0 + 16 * tw + r4;
   for (int ch = 0; ch < nchunks; ch++) {
@@ -820,6 +868,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
     lds_barrier();                       // B1
+    if (ch + 1 < nchunks) store_v(nb);    // every wave is past this chunk's V^T
     // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
     if (lw < NRT) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -830,6 +879,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
     lds_barrier();                       // B2
+    if (ch + 1 < nchunks) store_tt(nb);   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT) {
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
@@ -861,7 +911,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     // done with this chunk's staged data)
     if (ch + 1 < nchunks) {
       if (!DB) lds_barrier();
-      store_chunk(nb);
+      store_rest(nb);
     }
   }
 
