@@ -647,6 +647,37 @@ __device__ __forceinline__ f32x4 tile_mma_rt(f32x4 acc, const typename E::store_
   return acc;
 }
 
+// X = K S and Y = S^T Q^T for one 16-token row tile (fp32 operands, K a
+// multiple of 32), with the regrouped reads of tile_mma_f32: the S^T row a
+// lane reads is B for X and A for Y, so it is read once for both, and the
+// two independent chains interleave.  Reads go in batches of 4 k blocks.
+template <int K>
+__device__ __forceinline__ void tile_mma_xy_f32(f32x4& X, f32x4& Y, const float* Kr, const float* St,
+                                                const float* Qr, int ld, int lane) {
+  static_assert(K % 64 == 0 || K == 32, "K");
+  constexpr int NB = K >= 64 ? 4 : 2;  // k blocks of 16 per batch
+  const int r = lane & 15, kq = (lane >> 4) * 4;
+  const float *pk = Kr + r * ld + kq, *ps = St + r * ld + kq, *pq = Qr + r * ld + kq;
+#pragma unroll
+  for (int kb = 0; kb < K; kb += 16 * NB) {
+    f32x4 k4[NB], s4[NB], q4[NB];
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      k4[j] = *reinterpret_cast<const f32x4*>(pk + kb + 16 * j);
+      s4[j] = *reinterpret_cast<const f32x4*>(ps + kb + 16 * j);
+      q4[j] = *reinterpret_cast<const f32x4*>(pq + kb + 16 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NB; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        X = mfma16(k4[j][i], s4[j][i], X);
+        Y = mfma16(s4[j][i], q4[j][i], Y);
+      }
+  }
+}
+
 // Store 4 consecutive values (one lane's accumulator column) contiguously.
 __device__ __forceinline__ void st4(uint16_t* p, f32x4 v) {
   u32x2 w = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
@@ -860,10 +891,19 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     lds_barrier();                       // B0: staged chunk and S^T visible
     if (ch + 1 < nchunks) load_chunk(ch + 1);
 
-    // ---- X = K S, R = V - diag(a) X -> R^T
+    // ---- X = K S, R = V - diag(a) X -> R^T; and Y = S^T Q^T for the
+    // output, which needs only the chunk's start state
+    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
     if (lw < NRT) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      X = tile_mma<E, DK, true>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
+      if constexpr (E::KSTEP == 4) {
+        tile_mma_xy_f32<DK>(X, Y, reinterpret_cast<const float*>(&sm.k[b][16 * lw][0]),
+                            reinterpret_cast<const float*>(&sm.st[sb][tw][0][0]),
+                            reinterpret_cast<const float*>(&sm.q[b][16 * lw][0]), KLD, lane);
+      } else {
+        X = tile_mma<E, DK, true>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
+        Y = tile_mma<E, DK, true>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
+      }
       const int s = 16 * lw + r4;
       st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
@@ -882,8 +922,6 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     if (ch + 1 < nchunks) store_tt(nb);   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT) {
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      Y = tile_mma<E, DK, true>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 PU = {0.f, 0.f, 0.f, 0.f};
       PU = tile_mma_rt<E, C>(PU, &sm.ut[tw][0][0], CLD, &sm.p[b][16 * lw][0], CLD, lane, kend);
