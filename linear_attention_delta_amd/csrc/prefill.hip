@@ -686,17 +686,23 @@ __device__ __forceinline__ void st4(uint16_t* p, f32x4 v) {
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
 
-template <class E, int C, int DK, int NT, bool DB>
-__global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
+// SPLIT (one column tile, NT = 1): eight waves, two per SIMD.  Waves 0-3
+// carry as above (X, R, U and the state update); waves 4-7 form the output
+// (S^T Q^T beside X, then U^T P^T and the o store beside the state update),
+// so each phase's products are shared by two waves of a SIMD.
+template <class E, int C, int DK, int NT, bool DB, bool SPLIT>
+__global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a) {
+  static_assert(!SPLIT || NT == 1, "the split form has one column tile");
   typedef typename E::store_t T;
   typedef ScanSmem<E, C, DK, NT, DB> SM;
-  constexpr int NTH = 256 * NT;    // threads
+  constexpr int NTH = 256 * NT * (SPLIT ? 2 : 1);  // threads
   constexpr int NRT = C / 16;      // 16-row tiles per chunk
   constexpr int STW = DK / 64;     // state row tiles per wave (per column tile)
   constexpr int KLD = SM::KLD, CLD = SM::CLD;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int tw = wave >> 2, lw = wave & 3;   // column tile, wave within it
+  const int tw = SPLIT ? 0 : wave >> 2, lw = wave & 3;   // column tile, wave within it
+  const bool outw = SPLIT && wave >= 4;                 // an output wave of the split form
   const int c16 = lane & 15, r4 = (lane >> 4) * 4;
 
   // Zero all LDS once: the upper triangles and the K-step padding are read
@@ -753,8 +759,10 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
 #pragma unroll
       for (int t = 0; t < STW; t++) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (!outw) {
 #pragma unroll
-    for (int t = 0; t < STW; t++) st4(&sm.st[0][tw][c16][(lw * STW + t) * 16 + r4], S[t]);
+      for (int t = 0; t < STW; t++) st4(&sm.st[0][tw][c16][(lw * STW + t) * 16 + r4], S[t]);
+    }
   }
 
   // ---- staging: all global loads of a chunk are issued at once into
@@ -896,7 +904,10 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     f32x4 Y = {0.f, 0.f, 0.f, 0.f};
     if (lw < NRT) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (E::KSTEP == 4) {
+      if constexpr (SPLIT) {
+        if (!outw) X = tile_mma<E, DK, true>(X, &sm.k[b][16 * lw][0], KLD, &sm.st[sb][tw][0][0], KLD, lane);
+        else Y = tile_mma<E, DK, true>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
+      } else if constexpr (E::KSTEP == 4) {
         tile_mma_xy_f32<DK>(X, Y, reinterpret_cast<const float*>(&sm.k[b][16 * lw][0]),
                             reinterpret_cast<const float*>(&sm.st[sb][tw][0][0]),
                             reinterpret_cast<const float*>(&sm.q[b][16 * lw][0]), KLD, lane);
@@ -905,12 +916,12 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
         Y = tile_mma<E, DK, true>(Y, &sm.st[sb][tw][0][0], KLD, &sm.q[b][16 * lw][0], KLD, lane);
       }
       const int s = 16 * lw + r4;
-      st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
+      if (!outw) st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
     lds_barrier();                       // B1
     if (ch + 1 < nchunks) store_v(nb);    // every wave is past this chunk's V^T
     // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
-    if (lw < NRT) {
+    if (lw < NRT && !outw) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 U = {0.f, 0.f, 0.f, 0.f};
       U = tile_mma_rt<E, C>(U, &sm.tt[b][16 * lw][0], CLD, &sm.rt[tw][0][0], CLD, lane, kend);
@@ -921,7 +932,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
     lds_barrier();                       // B2
     if (ch + 1 < nchunks) store_tt(nb);   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
-    if (lw < NRT) {
+    if (lw < NRT && (!SPLIT || outw)) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
       f32x4 PU = {0.f, 0.f, 0.f, 0.f};
       PU = tile_mma_rt<E, C>(PU, &sm.ut[tw][0][0], CLD, &sm.p[b][16 * lw][0], CLD, lane, kend);
@@ -929,7 +940,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
       if (r < clen) st4(obase + (long)(cs + r) * a.hv * a.dv, sm.sc[b][1][r] * Y + PU);
     }
     // ---- S <- e^{gamma_last} S + K^T diag(c) U  -> S^T operand for the next chunk
-    {
+    if (!outw) {
       const float gl = sm.sc[b][3][0];
 #pragma unroll
       for (int t = 0; t < STW; t++) {
@@ -954,7 +965,7 @@ __global__ void __launch_bounds__(256 * NT) k_scan(ScanArgs a) {
   }
 
   // ---- final state
-  if (a.state_out) {
+  if (a.state_out && !outw) {
     float* so = a.state_out + ((long)seq * a.hv + h) * DK * a.dv;
     const int col = dv0 + 16 * tw + c16;
 #pragma unroll
@@ -987,14 +998,15 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   constexpr bool BF = std::is_same<E, BF16>::value;
   // Sequential carry for what the segment-parallel path does not take:
   // bf16 chunk 16 with two 16-column tiles per workgroup (8 waves), LDS
-  // double-buffered; fp32 with one tile (4 waves), single-buffered (the fp32
-  // tiles fill the LDS)
+  // double-buffered; fp32 with one tile (8 waves, the split form),
+  // single-buffered (the fp32 tiles fill the LDS)
   constexpr int NT = BF ? 2 : 1;
+  constexpr bool SPLIT = !BF;  // fp32: eight waves per tile, the output formed by waves of its own
   const int GS = (a.hv / a.hk) * (a.dv / (16 * NT));
   const int ngroups = a.num_seqs * a.hk;
   const int per_xcd = (ngroups + 7) / 8;
-  dim3 grid(8 * per_xcd * GS), block(256 * NT);
-  hipLaunchKernelGGL((k_scan<E, C, DK, NT, BF>), grid, block, 0, s, a);
+  dim3 grid(8 * per_xcd * GS), block(256 * NT * (SPLIT ? 2 : 1));
+  hipLaunchKernelGGL((k_scan<E, C, DK, NT, BF, SPLIT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
