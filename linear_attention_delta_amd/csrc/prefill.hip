@@ -783,7 +783,16 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   const T* vp = reinterpret_cast<const T*>(a.v);
   const T* mp = reinterpret_cast<const T*>(a.tinv);
   const float* scp = a.scal;
-  u32x4 pkq[NKQ], pm[NM], pv = {0u, 0u, 0u, 0u}, ps = {0u, 0u, 0u, 0u};
+  // Register sets of staged loads: with one LDS buffer, two sets, so that a
+  // chunk's loads are issued two chunks ahead of its use (one chunk's
+  // compute was too short for them to land).  Set indices are compile-time
+  // (the chunk loop runs in pairs), so the sets stay in registers.
+  constexpr int PF = DB ? 1 : 2;
+  struct Staged {
+    u32x4 kq[NKQ], m[NM], v, s;
+    int len;  // valid rows of the chunk held
+  };
+  Staged rs[PF];
   // Each thread's element offsets, computed once: a chunk's load is its base
   // plus the offset, with no 64-bit row-times-stride product per vector.
   // Every load is unconditional (a load inside a branch makes the compiler
@@ -807,19 +816,18 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     v0 = h * a.dv + dv0 + cv * EPV;
     vo = (long)r * a.stride_v + v0;
   }
-  int staged_len = C;  // valid rows of the chunk held in the registers
-
-  auto load_chunk = [&](int ch) {
+  auto load_chunk = [&](int ch, auto set_) {
+    Staged& R = rs[decltype(set_)::value];
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
-    staged_len = clen;
+    R.len = clen;
     // in the order the stores below consume them (the load counter retires
     // in order): V, then Tt and P, then K and Q, then the scalars
-    pv = *reinterpret_cast<const u32x4*>(vp + (long)cs * a.stride_v + (vr < clen ? vo : (long)v0));
+    R.v = *reinterpret_cast<const u32x4*>(vp + (long)cs * a.stride_v + (vr < clen ? vo : (long)v0));
     const long blk = (long)(cbase + ch) * a.hv + h;
     const T* msrc = mp + blk * (2 * C * C);
 #pragma unroll
-    for (int j = 0; j < NM; j++) pm[j] = *reinterpret_cast<const u32x4*>(msrc + min(tid + NTH * j, M_V - 1) * EPV);
+    for (int j = 0; j < NM; j++) R.m[j] = *reinterpret_cast<const u32x4*>(msrc + min(tid + NTH * j, M_V - 1) * EPV);
     const T* kc = kp + (long)cs * a.stride_k;
     const T* qc = qp + (long)cs * a.stride_q;
 #pragma unroll
@@ -827,49 +835,52 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       const int idx = tid + NTH * j;
       const int which = idx / (C * VPR);
       const T* src = (which ? qc : kc) + (kqr[j] < clen ? kqo[j] : (long)kq0[j]);
-      pkq[j] = *reinterpret_cast<const u32x4*>(src);
+      R.kq[j] = *reinterpret_cast<const u32x4*>(src);
     }
-    ps = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
+    R.s = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
   };
 
   // The next chunk's staging goes in three parts, each as soon as no wave
   // reads that array of the current chunk any more (in a single buffer):
   // V^T once every wave is past R (after B1), Tt once every wave is past U
   // (after B2), and the rest at the end of the chunk.
-  auto store_v = [&](int b) {
-    if (staged_len < C) {
+  auto store_v = [&](int b, auto set_) {
+    Staged& R = rs[decltype(set_)::value];
+    if (R.len < C) {
       // the sequence's last, partial chunk: rows past its end are zero (a
       // branch with no memory access, taken by every lane or none)
 #pragma unroll
       for (int j = 0; j < NKQ; j++)
-        if (kqr[j] >= staged_len) pkq[j] = u32x4{0u, 0u, 0u, 0u};
-      if (vr >= staged_len) pv = u32x4{0u, 0u, 0u, 0u};
+        if (kqr[j] >= R.len) R.kq[j] = u32x4{0u, 0u, 0u, 0u};
+      if (vr >= R.len) R.v = u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < V_V) {
       const int r = tid / V_VPR, cv = tid % V_VPR;
-      const T* e = reinterpret_cast<const T*>(&pv);
+      const T* e = reinterpret_cast<const T*>(&R.v);
 #pragma unroll
       for (int i = 0; i < EPV; i++) sm.vt[b][cv * EPV + i][r] = E::to_f32(e[i]);
     }
   };
-  auto store_tt = [&](int b) {
+  auto store_tt = [&](int b, auto set_) {
+    const Staged& R = rs[decltype(set_)::value];
 #pragma unroll
     for (int j = 0; j < NM; j++) {
       const int idx = tid + NTH * j;
       if (idx < C * C / EPV) {
         const int r = idx / (C / EPV), cv = idx % (C / EPV);
-        *reinterpret_cast<u32x4*>(&sm.tt[b][r][cv * EPV]) = pm[j];
+        *reinterpret_cast<u32x4*>(&sm.tt[b][r][cv * EPV]) = R.m[j];
       }
     }
   };
-  auto store_rest = [&](int b) {
+  auto store_rest = [&](int b, auto set_) {
+    const Staged& R = rs[decltype(set_)::value];
 #pragma unroll
     for (int j = 0; j < NKQ; j++) {
       const int idx = tid + NTH * j;
       const int which = idx / (C * VPR);
       const int rem = idx % (C * VPR);
       const int r = rem / VPR, cv = rem % VPR;
-      if (idx < KQ_V) *reinterpret_cast<u32x4*>(which ? &sm.q[b][r][cv * EPV] : &sm.k[b][r][cv * EPV]) = pkq[j];
+      if (idx < KQ_V) *reinterpret_cast<u32x4*>(which ? &sm.q[b][r][cv * EPV] : &sm.k[b][r][cv * EPV]) = R.kq[j];
     }
 #pragma unroll
     for (int j = 0; j < NM; j++) {
@@ -877,27 +888,36 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       if (idx >= C * C / EPV && idx < M_V) {
         const int rem = idx - C * C / EPV;
         const int r = rem / (C / EPV), cv = rem % (C / EPV);
-        *reinterpret_cast<u32x4*>(&sm.p[b][r][cv * EPV]) = pm[j];
+        *reinterpret_cast<u32x4*>(&sm.p[b][r][cv * EPV]) = R.m[j];
       }
     }
-    if (tid < S_V) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + tid * 4) = ps;
+    if (tid < S_V) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + tid * 4) = R.s;
   };
 
+  typedef std::integral_constant<int, 0> Set0;
+  typedef std::integral_constant<int, PF - 1> Set1;  // the second set (the first when PF = 1)
   if (nchunks > 0) {
-    load_chunk(0);
-    store_v(0);
-    store_tt(0);
-    store_rest(0);
+    load_chunk(0, Set0());
+    if (PF == 2 && nchunks > 1) load_chunk(1, Set1());
+    store_v(0, Set0());
+    store_tt(0, Set0());
+    store_rest(0, Set0());
   }
   T* obase = reinterpret_cast<T*>(a.o) + (long)h * a.dv + dv0 + 16 * tw + r4;
-  for (int ch = 0; ch < nchunks; ch++) {
+  // One chunk; with PF = 2, chunk ch's loads went to set ch % 2 and its
+  // chunk + 2 loads go there again once it is stored (at the end of chunk
+  // ch - 1), chunk ch + 1 is stored from the other set.
+  auto chunk_step = [&](int ch, auto par_) {
+    constexpr int P = decltype(par_)::value;
+    typedef std::integral_constant<int, PF == 2 ? P : 0> LoadSet;
+    typedef std::integral_constant<int, PF == 2 ? 1 - P : 0> StoreSet;
     const int b = DB ? (ch & 1) : 0;
     const int nb = DB ? (b ^ 1) : 0;
     const int sb = ch & 1;                 // state operand buffer read this chunk
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
     lds_barrier();                       // B0: staged chunk and S^T visible
-    if (ch + 1 < nchunks) load_chunk(ch + 1);
+    if (ch + PF < nchunks) load_chunk(ch + PF, LoadSet());
 
     // ---- X = K S, R = V - diag(a) X -> R^T; and Y = S^T Q^T for the
     // output, which needs only the chunk's start state
@@ -919,7 +939,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       if (!outw) st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
     lds_barrier();                       // B1
-    if (ch + 1 < nchunks) store_v(nb);    // every wave is past this chunk's V^T
+    if (ch + 1 < nchunks) store_v(nb, StoreSet());    // every wave is past this chunk's V^T
     // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
     if (lw < NRT && !outw) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -930,7 +950,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
     lds_barrier();                       // B2
-    if (ch + 1 < nchunks) store_tt(nb);   // every wave is past this chunk's Tt
+    if (ch + 1 < nchunks) store_tt(nb, StoreSet());   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT && (!SPLIT || outw)) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -960,8 +980,12 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     // done with this chunk's staged data)
     if (ch + 1 < nchunks) {
       if (!DB) lds_barrier();
-      store_rest(nb);
+      store_rest(nb, StoreSet());
     }
+  };
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    chunk_step(ch, std::integral_constant<int, 0>());
+    if (ch + 1 < nchunks) chunk_step(ch + 1, std::integral_constant<int, 1>());
   }
 
   // ---- final state
