@@ -545,11 +545,12 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
 
 // ---------------------------------------------------------------- phase 2
 //
-// One workgroup per (sequence, v-head, NT*16 columns of d_v), 4*NT waves.
-// Waves 4t..4t+3 own column tile t; within it wave lw owns token rows
-// 16lw..16lw+15 of the chunk (X, U, O) and d_k rows of the state (S).
-// Per chunk (staged data in LDS buffer b, the next chunk's loads in flight):
-//   B0 | X = K S -> R | B1 | U = Tt R | B2 | O^T = diag(b) S^T Q^T + U^T P^T ;
+// One workgroup per (sequence, v-head, NT*16 columns of d_v), 4*NT waves
+// (8 for the split form below).  Waves 4t..4t+3 own column tile t; within it
+// wave lw owns token rows 16lw..16lw+15 of the chunk (X, U, O) and d_k rows
+// of the state (S).  Per chunk (staged data in LDS buffer b, the next
+// chunks' loads in flight):
+//   B0 | X = K S -> R, S^T Q^T | B1 | U = Tt R | B2 | O^T = diag(b) S^T Q^T + U^T P^T ;
 //        S <- e^{gl} S + K^T diag(c) U ; stage next chunk
 // O is formed transposed so each lane owns 4 consecutive columns of one
 // token row and writes them with one 8- or 16-byte store.
