@@ -49,7 +49,8 @@ struct ScanArgs {
   float* state_out;
   // workspace carve-up
   int32_t* chunk_offsets;     // [num_seqs + 1], varlen only
-  void* tinv;                 // [max_chunks][hv][2][chunk][chunk] in the operand type: Tt, P
+  void* tinv;                 // [max_chunks][hv][2][chunk][chunk] in the operand type: Tt, P, each as
+                              // its lower 16x16 blocks packed at the front (block i(i+1)/2+j at 256 n)
   float* scal;                // [max_chunks][hv][kScalRows][chunk] fp32 per-row scalars (see kScalRows)
   int max_chunks;
   // segment-parallel scan (bf16, chunk 32/64): every sequence is cut into

@@ -378,26 +378,13 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
         const float val = fr * rks[e] * __expf(gr - gs[e]) * acc[e];
         v[e] = s0 + e <= r ? val : 0.f;
       }
-      T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C;
+      // packed like Tt: lower block t (row-major, 256 values) at 256 t
+      T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C + 256 * t +
+                16 * c16 + r4;
       if constexpr (std::is_same<E, BF16>::value) {
-        *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(pout) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
       } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(pout) + r * C + s0) = v;
-      }
-    }
-  }
-  // upper tiles of P are zero (the scan reads P in whole 32-column steps)
-  for (int t = wave; t < NRT * NRT; t += PW) {
-    const int i = t / NRT, j = t % NRT;
-    if (j <= i) continue;
-    const int r = 16 * i + c16, s0 = 16 * j + r4;
-#pragma unroll
-    for (int hh = 0; hh < HPW; hh++) {
-      T* pout = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C) + C * C;
-      if constexpr (std::is_same<E, BF16>::value) {
-        *reinterpret_cast<u32x2*>(pout + r * C + s0) = u32x2{0u, 0u};
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(pout) + r * C + s0) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(pout) = v;
       }
     }
   }
@@ -491,11 +478,12 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
     }
     lds_barrier();
   }
-  // ---- Tt = inv diag(beta), upper triangle zero, to the workspace.  For the
-  // segment-parallel carry only its lower 16x16 blocks are stored, packed:
-  // block n = i(i+1)/2 + j (row tile i, column tile j <= i) is 256 values,
-  // row-major, at 256 n.  The sequential carry reads the full C x C matrix.
-  if constexpr (!WQ) {
+  // ---- Tt = inv diag(beta), upper triangle zero, to the workspace: only its
+  // lower 16x16 blocks, packed: block n = i(i+1)/2 + j (row tile i, column
+  // tile j <= i) is 256 values, row-major, at 256 n (P the same, C x C
+  // further on).  The carries place the blocks in LDS, whose upper blocks
+  // stay zero.
+  {
 #pragma unroll
     for (int hh = 0; hh < HPW; hh++) {
       T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);
@@ -520,24 +508,6 @@ __global__ void __launch_bounds__(64 * kPrepWaves) k_prepare(ScanArgs a) {
           *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
         }
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int hh = 0; hh < HPW; hh++) {
-    T* out = reinterpret_cast<T*>(a.tinv) + (chunk * a.hv + hs[hh]) * (2 * C * C);
-    for (int idx = tid; idx < C * C / 4; idx += PT) {
-      const int r = idx / (C / 4), s0 = (idx % (C / 4)) * 4;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.u.at[hh][r][s0]);
-      const f32x4 bs = *reinterpret_cast<const f32x4*>(&sm.bet[hh][s0]);
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; e++) v[e] = s0 + e <= r ? x[e] * bs[e] : 0.f;
-      if constexpr (std::is_same<E, BF16>::value) {
-        *reinterpret_cast<u32x2*>(out + r * C + s0) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + r * C + s0) = v;
       }
     }
   }
@@ -773,7 +743,10 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   constexpr int VPR = DK / EPV;                    // vectors per K/Q row
   constexpr int KQ_V = 2 * C * VPR;                // K and Q vectors per chunk
   constexpr int NKQ = (KQ_V + NTH - 1) / NTH;
-  constexpr int M_V = 2 * C * C / EPV;             // Tt and P vectors per chunk
+  constexpr int NTB = NRT * (NRT + 1) / 2;         // lower 16x16 blocks of Tt (and of P)
+  constexpr int BV = 256 / EPV;                    // vectors per block
+  constexpr int MH_V = NTB * BV;                   // Tt vectors per chunk (P the same)
+  constexpr int M_V = 2 * MH_V;
   constexpr int NM = (M_V + NTH - 1) / NTH;
   constexpr int V_VPR = 16 * NT / EPV;             // V vectors per row
   constexpr int V_V = C * V_VPR;
@@ -801,6 +774,21 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   // sequence's end reads the chunk's first row and is zeroed at the store.
   long kqo[NKQ], vo = 0;
   int kq0[NKQ], kqr[NKQ], v0 = 0, vr = C;
+  // Tt and P arrive as their lower blocks, packed (block n = i(i+1)/2 + j at
+  // 256 n, row-major; P at C x C): each vector's source and its place in the
+  // LDS matrix, whose upper blocks keep the zeros written above
+  int mo[NM], ml[NM];
+#pragma unroll
+  for (int j = 0; j < NM; j++) {
+    const int idx = min(tid + NTH * j, M_V - 1);
+    const int isp = idx >= MH_V, rem = idx - isp * MH_V;
+    const int n = rem / BV, w = rem % BV;
+    int bi = 0;
+    while ((bi + 1) * (bi + 2) / 2 <= n) bi++;
+    const int bj = n - bi * (bi + 1) / 2;
+    mo[j] = isp * C * C + rem * EPV;
+    ml[j] = (16 * bi + w / (16 / EPV)) * CLD + 16 * bj + (w % (16 / EPV)) * EPV;
+  }
 #pragma unroll
   for (int j = 0; j < NKQ; j++) {
     const int idx = tid + NTH * j;
@@ -828,7 +816,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     const long blk = (long)(cbase + ch) * a.hv + h;
     const T* msrc = mp + blk * (2 * C * C);
 #pragma unroll
-    for (int j = 0; j < NM; j++) R.m[j] = *reinterpret_cast<const u32x4*>(msrc + min(tid + NTH * j, M_V - 1) * EPV);
+    for (int j = 0; j < NM; j++) R.m[j] = *reinterpret_cast<const u32x4*>(msrc + mo[j]);
     const T* kc = kp + (long)cs * a.stride_k;
     const T* qc = qp + (long)cs * a.stride_q;
 #pragma unroll
@@ -865,13 +853,8 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   auto store_tt = [&](int b, auto set_) {
     const Staged& R = rs[decltype(set_)::value];
 #pragma unroll
-    for (int j = 0; j < NM; j++) {
-      const int idx = tid + NTH * j;
-      if (idx < C * C / EPV) {
-        const int r = idx / (C / EPV), cv = idx % (C / EPV);
-        *reinterpret_cast<u32x4*>(&sm.tt[b][r][cv * EPV]) = R.m[j];
-      }
-    }
+    for (int j = 0; j < NM; j++)
+      if (tid + NTH * j < MH_V) *reinterpret_cast<u32x4*>(&sm.tt[b][0][0] + ml[j]) = R.m[j];
   };
   auto store_rest = [&](int b, auto set_) {
     const Staged& R = rs[decltype(set_)::value];
@@ -886,11 +869,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
 #pragma unroll
     for (int j = 0; j < NM; j++) {
       const int idx = tid + NTH * j;
-      if (idx >= C * C / EPV && idx < M_V) {
-        const int rem = idx - C * C / EPV;
-        const int r = rem / (C / EPV), cv = rem % (C / EPV);
-        *reinterpret_cast<u32x4*>(&sm.p[b][r][cv * EPV]) = R.m[j];
-      }
+      if (idx >= MH_V && idx < M_V) *reinterpret_cast<u32x4*>(&sm.p[b][0][0] + ml[j]) = R.m[j];
     }
     if (tid < S_V) *reinterpret_cast<u32x4*>(&sm.sc[b][0][0] + tid * 4) = R.s;
   };
