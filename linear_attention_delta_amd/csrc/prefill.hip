@@ -772,8 +772,29 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   // Every load is unconditional (a load inside a branch makes the compiler
   // wait for the loads in flight where the branch rejoins): a row past the
   // sequence's end reads the chunk's first row and is zeroed at the store.
-  long kqo[NKQ], vo = 0;
-  int kq0[NKQ], kqr[NKQ], v0 = 0, vr = C;
+  //
+  // K and Q: a thread's vector j is row r0 + RS j of the 2C rows [K; Q], in
+  // a fixed column, so the thread keeps one row offset per matrix and the
+  // rest of each vector's offset is uniform.
+  constexpr int RS = NTH / VPR;                    // rows one vector per thread covers
+  constexpr bool ROWSTEP = C % RS == 0;            // else RS is a multiple of C
+  static_assert(NTH % VPR == 0 && (ROWSTEP || RS % C == 0), "staging");
+  const int r0 = tid / VPR;
+  const int kqc = hk * DK + (tid % VPR) * EPV;    // this thread's column
+  // matrix (0 K, 1 Q, 2 or more: no vector) and row of vector j
+  auto kq_at = [&](int j, int& which, int& r) {
+    if constexpr (ROWSTEP) {
+      which = RS * j / C;
+      r = r0 + (RS * j) % C;
+    } else {
+      which = (r0 + RS * j) / C;
+      r = r0 % C;
+    }
+  };
+  const int rb0 = ROWSTEP ? r0 : r0 % C;
+  const long rk0 = (long)rb0 * a.stride_k, rq0 = (long)rb0 * a.stride_q;
+  long vo = 0;
+  int v0 = 0, vr = C;
   // Tt and P arrive as their lower blocks, packed (block n = i(i+1)/2 + j at
   // 256 n, row-major; P at C x C): each vector's source and its place in the
   // LDS matrix, whose upper blocks keep the zeros written above
@@ -788,16 +809,6 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     const int bj = n - bi * (bi + 1) / 2;
     mo[j] = isp * C * C + rem * EPV;
     ml[j] = (16 * bi + w / (16 / EPV)) * CLD + 16 * bj + (w % (16 / EPV)) * EPV;
-  }
-#pragma unroll
-  for (int j = 0; j < NKQ; j++) {
-    const int idx = tid + NTH * j;
-    const int which = idx / (C * VPR);
-    const int rem = idx % (C * VPR);
-    const int r = rem / VPR, cv = rem % VPR;
-    kqr[j] = idx < KQ_V ? r : C;
-    kq0[j] = hk * DK + cv * EPV;
-    kqo[j] = (long)r * (which ? a.stride_q : a.stride_k) + kq0[j];
   }
   if (tid < V_V) {
     const int r = tid / V_VPR, cv = tid % V_VPR;
@@ -821,9 +832,11 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     const T* qc = qp + (long)cs * a.stride_q;
 #pragma unroll
     for (int j = 0; j < NKQ; j++) {
-      const int idx = tid + NTH * j;
-      const int which = idx / (C * VPR);
-      const T* src = (which ? qc : kc) + (kqr[j] < clen ? kqo[j] : (long)kq0[j]);
+      int which, r;
+      kq_at(j, which, r);
+      const int dr = ROWSTEP ? (RS * j) % C : 0;  // uniform row step
+      const long ro = which == 1 ? rq0 + (long)dr * a.stride_q : rk0 + (long)dr * a.stride_k;
+      const T* src = (which == 1 ? qc : kc) + ((which < 2 && r < clen) ? ro : 0) + kqc;
       R.kq[j] = *reinterpret_cast<const u32x4*>(src);
     }
     R.s = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
@@ -839,8 +852,11 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       // the sequence's last, partial chunk: rows past its end are zero (a
       // branch with no memory access, taken by every lane or none)
 #pragma unroll
-      for (int j = 0; j < NKQ; j++)
-        if (kqr[j] >= R.len) R.kq[j] = u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NKQ; j++) {
+        int which, r;
+        kq_at(j, which, r);
+        if (r >= R.len) R.kq[j] = u32x4{0u, 0u, 0u, 0u};
+      }
       if (vr >= R.len) R.v = u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < V_V) {
@@ -858,13 +874,12 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   };
   auto store_rest = [&](int b, auto set_) {
     const Staged& R = rs[decltype(set_)::value];
+    const int cve = (tid % VPR) * EPV;
 #pragma unroll
     for (int j = 0; j < NKQ; j++) {
-      const int idx = tid + NTH * j;
-      const int which = idx / (C * VPR);
-      const int rem = idx % (C * VPR);
-      const int r = rem / VPR, cv = rem % VPR;
-      if (idx < KQ_V) *reinterpret_cast<u32x4*>(which ? &sm.q[b][r][cv * EPV] : &sm.k[b][r][cv * EPV]) = R.kq[j];
+      int which, r;
+      kq_at(j, which, r);
+      if (which < 2) *reinterpret_cast<u32x4*>(which ? &sm.q[b][r][cve] : &sm.k[b][r][cve]) = R.kq[j];
     }
 #pragma unroll
     for (int j = 0; j < NM; j++) {
@@ -878,7 +893,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   typedef std::integral_constant<int, PF - 1> Set1;  // the second set (the first when PF = 1)
   if (nchunks > 0) {
     load_chunk(0, Set0());
-    if (PF == 2 && nchunks > 1) load_chunk(1, Set1());
+    if (PF == 2) load_chunk(min(1, nchunks - 1), Set1());
     store_v(0, Set0());
     store_tt(0, Set0());
     store_rest(0, Set0());
@@ -897,7 +912,11 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
     lds_barrier();                       // B0: staged chunk and S^T visible
-    if (ch + PF < nchunks) load_chunk(ch + PF, LoadSet());
+    // Unconditional: past the last chunk it loads the last one again, into a
+    // set that is never stored.  (Under a branch the compiler would count
+    // these loads as maybe not issued and wait for the newest of them where
+    // the older set is stored.)
+    load_chunk(min(ch + PF, nchunks - 1), LoadSet());
 
     // ---- X = K S, R = V - diag(a) X -> R^T; and Y = S^T Q^T for the
     // output, which needs only the chunk's start state
@@ -963,9 +982,12 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       store_rest(nb, StoreSet());
     }
   };
+  // in pairs; an odd last chunk leaves the loop between the two, so that the
+  // loop's back edge comes only from a full pair (the same reason)
   for (int ch = 0; ch < nchunks; ch += 2) {
     chunk_step(ch, std::integral_constant<int, 0>());
-    if (ch + 1 < nchunks) chunk_step(ch + 1, std::integral_constant<int, 1>());
+    if (ch + 1 >= nchunks) break;
+    chunk_step(ch + 1, std::integral_constant<int, 1>());
   }
 
   // ---- final state
