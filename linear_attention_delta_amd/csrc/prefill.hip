@@ -816,31 +816,50 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     v0 = h * a.dv + dv0 + cv * EPV;
     vo = (long)r * a.stride_v + v0;
   }
-  auto load_chunk = [&](int ch, auto set_) {
+  // A chunk's loads by a flat index, in the order the stores below consume
+  // them (the load counter retires in order): V (0), Tt and P (1 .. NM), K
+  // and Q (NM + 1 .. NM + NKQ), the scalars (NM + NKQ + 1); load_part issues
+  // those in [LO, HI).
+  constexpr int NLD = NM + NKQ + 2;
+  auto load_part = [&](int ch, auto set_, auto lo_, auto hi_) {
+    constexpr int LO = decltype(lo_)::value, HI = decltype(hi_)::value;
     Staged& R = rs[decltype(set_)::value];
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
-    R.len = clen;
-    // in the order the stores below consume them (the load counter retires
-    // in order): V, then Tt and P, then K and Q, then the scalars
-    R.v = *reinterpret_cast<const u32x4*>(vp + (long)cs * a.stride_v + (vr < clen ? vo : (long)v0));
     const long blk = (long)(cbase + ch) * a.hv + h;
+    if constexpr (LO == 0 && HI > 0) {
+      R.len = clen;
+      R.v = *reinterpret_cast<const u32x4*>(vp + (long)cs * a.stride_v + (vr < clen ? vo : (long)v0));
+    }
     const T* msrc = mp + blk * (2 * C * C);
 #pragma unroll
-    for (int j = 0; j < NM; j++) R.m[j] = *reinterpret_cast<const u32x4*>(msrc + mo[j]);
+    for (int j = 0; j < NM; j++)
+      if (LO <= 1 + j && 1 + j < HI) R.m[j] = *reinterpret_cast<const u32x4*>(msrc + mo[j]);
     const T* kc = kp + (long)cs * a.stride_k;
     const T* qc = qp + (long)cs * a.stride_q;
 #pragma unroll
     for (int j = 0; j < NKQ; j++) {
-      int which, r;
-      kq_at(j, which, r);
-      const int dr = ROWSTEP ? (RS * j) % C : 0;  // uniform row step
-      const long ro = which == 1 ? rq0 + (long)dr * a.stride_q : rk0 + (long)dr * a.stride_k;
-      const T* src = (which == 1 ? qc : kc) + ((which < 2 && r < clen) ? ro : 0) + kqc;
-      R.kq[j] = *reinterpret_cast<const u32x4*>(src);
+      if (LO <= 1 + NM + j && 1 + NM + j < HI) {
+        int which, r;
+        kq_at(j, which, r);
+        const int dr = ROWSTEP ? (RS * j) % C : 0;  // uniform row step
+        const long ro = which == 1 ? rq0 + (long)dr * a.stride_q : rk0 + (long)dr * a.stride_k;
+        const T* src = (which == 1 ? qc : kc) + ((which < 2 && r < clen) ? ro : 0) + kqc;
+        R.kq[j] = *reinterpret_cast<const u32x4*>(src);
+      }
     }
-    R.s = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
+    if constexpr (LO <= NLD - 1 && NLD - 1 < HI)
+      R.s = *reinterpret_cast<const u32x4*>(scp + blk * (kScalRows * C) + min(tid, S_V - 1) * 4);
   };
+  typedef std::integral_constant<int, 0> LdFirst;
+  typedef std::integral_constant<int, NLD> LdAll;
+  // With two register sets, the loads two chunks ahead go out in parts
+  // between the phases, none in the first, whose products both waves of
+  // each SIMD run (issued there, they held up those products): from LD1 on
+  // after U's barrier, V, Tt and P before (a burst of all of them in one
+  // place cost more).
+  constexpr int LD1 = 1 + NM;
+  typedef std::integral_constant<int, LD1> LdSplit1;
 
   // The next chunk's staging goes in three parts, each as soon as no wave
   // reads that array of the current chunk any more (in a single buffer):
@@ -892,8 +911,8 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   typedef std::integral_constant<int, 0> Set0;
   typedef std::integral_constant<int, PF - 1> Set1;  // the second set (the first when PF = 1)
   if (nchunks > 0) {
-    load_chunk(0, Set0());
-    if (PF == 2) load_chunk(min(1, nchunks - 1), Set1());
+    load_part(0, Set0(), LdFirst(), LdAll());
+    if (PF == 2) load_part(min(1, nchunks - 1), Set1(), LdFirst(), LdAll());
     store_v(0, Set0());
     store_tt(0, Set0());
     store_rest(0, Set0());
@@ -912,11 +931,9 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     const int cs = s0 + ch * C;
     const int clen = min(C, s1 - cs);
     lds_barrier();                       // B0: staged chunk and S^T visible
-    // Unconditional: past the last chunk it loads the last one again, into a
-    // set that is never stored.  (Under a branch the compiler would count
-    // these loads as maybe not issued and wait for the newest of them where
-    // the older set is stored.)
-    load_chunk(min(ch + PF, nchunks - 1), LoadSet());
+    // one register set: the next chunk's loads go out first, as it is stored
+    // during this chunk (unconditional, for the reason given below)
+    if constexpr (PF == 1) load_part(min(ch + 1, nchunks - 1), LoadSet(), LdFirst(), LdAll());
 
     // ---- X = K S, R = V - diag(a) X -> R^T; and Y = S^T Q^T for the
     // output, which needs only the chunk's start state
@@ -938,7 +955,14 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       if (!outw) st4(&sm.rt[tw][c16][s], ld4(&sm.vt[b][16 * tw + c16][s]) - ld4(&sm.sc[b][0][s]) * X);
     }
     lds_barrier();                       // B1
-    if (ch + 1 < nchunks) store_v(nb, StoreSet());    // every wave is past this chunk's V^T
+    // Two register sets: the first part of the loads two chunks ahead.
+    // Unconditional: past the last chunk they load the last one again, into
+    // a set that is never stored.  (Under a branch the compiler would count
+    // them as maybe not issued and wait for the newest of them where the
+    // older set is stored.)
+    const int lch = min(ch + 2, nchunks - 1);
+    if constexpr (PF == 2) load_part(lch, LoadSet(), LdFirst(), LdSplit1());
+    store_v(nb, StoreSet());    // every wave is past this chunk's V^T
     // ---- U = Tt R (Tt lower triangular: k < 16(lw+1)) -> U^T, (diag(c) U)^T
     if (lw < NRT && !outw) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -949,7 +973,8 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
     lds_barrier();                       // B2
-    if (ch + 1 < nchunks) store_tt(nb, StoreSet());   // every wave is past this chunk's Tt
+    if constexpr (PF == 2) load_part(lch, LoadSet(), LdSplit1(), LdAll());   // the rest
+    store_tt(nb, StoreSet());   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT && (!SPLIT || outw)) {
       const int kend = ((16 * (lw + 1) + E::KSTEP - 1) / E::KSTEP) * E::KSTEP;
@@ -976,14 +1001,14 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       }
     }
     // ---- stage the next chunk (single-buffered: wait until all waves are
-    // done with this chunk's staged data)
-    if (ch + 1 < nchunks) {
-      if (!DB) lds_barrier();
-      store_rest(nb, StoreSet());
-    }
+    // done with this chunk's staged data).  Like the loads, the stores have
+    // no branch around them: after the last chunk they write the last chunk
+    // again, which nothing reads.
+    if (!DB) lds_barrier();
+    store_rest(nb, StoreSet());
   };
-  // in pairs; an odd last chunk leaves the loop between the two, so that the
-  // loop's back edge comes only from a full pair (the same reason)
+  // in pairs (the register sets are compile-time); an odd last chunk leaves
+  // the loop between the two steps
   for (int ch = 0; ch < nchunks; ch += 2) {
     chunk_step(ch, std::integral_constant<int, 0>());
     if (ch + 1 >= nchunks) break;
