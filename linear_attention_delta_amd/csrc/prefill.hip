@@ -853,13 +853,16 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   };
   typedef std::integral_constant<int, 0> LdFirst;
   typedef std::integral_constant<int, NLD> LdAll;
-  // With two register sets, the loads two chunks ahead go out in parts
-  // between the phases, none in the first, whose products both waves of
-  // each SIMD run (issued there, they held up those products): from LD1 on
-  // after U's barrier, V, Tt and P before (a burst of all of them in one
-  // place cost more).
+  // With two register sets, the loads two chunks ahead go out in three
+  // parts between the phases, none in the first, whose products both waves
+  // of each SIMD run (issued there, they held up those products): V, Tt and
+  // P after its barrier, K and Q up to LD2 after U's, the last five at the
+  // end of the chunk.  (One burst anywhere cost more; the split points were
+  // measured on the 8192-token fp32 layer.)
   constexpr int LD1 = 1 + NM;
+  constexpr int LD2 = NLD - 5 > LD1 ? NLD - 5 : LD1;
   typedef std::integral_constant<int, LD1> LdSplit1;
+  typedef std::integral_constant<int, LD2> LdSplit2;
 
   // The next chunk's staging goes in three parts, each as soon as no wave
   // reads that array of the current chunk any more (in a single buffer):
@@ -973,7 +976,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
       st4(&sm.u2t[tw][c16][s], ld4(&sm.sc[b][2][s]) * U);
     }
     lds_barrier();                       // B2
-    if constexpr (PF == 2) load_part(lch, LoadSet(), LdSplit1(), LdAll());   // the rest
+    if constexpr (PF == 2) load_part(lch, LoadSet(), LdSplit1(), LdSplit2());
     store_tt(nb, StoreSet());   // every wave is past this chunk's Tt
     // ---- O^T = diag(b) (S^T Q^T) + U^T P^T, tokens 16lw..16lw+15
     if (lw < NRT && (!SPLIT || outw)) {
@@ -1004,6 +1007,7 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     // done with this chunk's staged data).  Like the loads, the stores have
     // no branch around them: after the last chunk they write the last chunk
     // again, which nothing reads.
+    if constexpr (PF == 2) load_part(lch, LoadSet(), LdSplit2(), LdAll());
     if (!DB) lds_barrier();
     store_rest(nb, StoreSet());
   };
