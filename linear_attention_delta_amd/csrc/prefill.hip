@@ -736,9 +736,9 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
     }
   }
 
-  // ---- staging: all global loads of a chunk are issued at once into
-  // registers one chunk ahead (per-thread source pointers are fixed; only a
-  // per-chunk offset moves), then written to LDS.
+  // ---- staging: a chunk's global loads go into registers ahead of its use
+  // (per-thread source offsets are fixed; only a per-chunk base moves), then
+  // are written to LDS in the parts its single buffer frees up.
   constexpr int EPV = 16 / sizeof(T);              // elements per 16-byte vector
   constexpr int VPR = DK / EPV;                    // vectors per K/Q row
   constexpr int KQ_V = 2 * C * VPR;                // K and Q vectors per chunk
