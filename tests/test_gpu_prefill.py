@@ -100,6 +100,27 @@ def test_ragged_varlen_all_heads(G, orc, dtype, chunk):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,chunk,dk,dv", [
+    ("f32", 16, 64, 128), ("f32", 32, 64, 64), ("f32", 16, 64, 64), ("f32", 32, 128, 64),
+    ("bf16", 16, 64, 128), ("bf16", 16, 64, 64)])
+def test_ragged_sequential_carry_shapes(G, orc, dtype, chunk, dk, dv):
+    """The sequential carry (fp32, and bf16 chunk 16) at d_k = 64 and small
+    chunks, where a thread's staged K/Q vectors cover rows of both matrices
+    and its loads split differently over the chunk: odd and even chunk
+    counts, a lone chunk, ragged tails and an empty sequence, with nonzero
+    initial states."""
+    sh = synth.LayerShape(2, 4, dk, dv)
+    inp = synth.make_prefill(31 + chunk + dk + dv, sh, [1, 17, 0, 33, 96, 130], dtype, state0_std=0.05,
+                             chunk_size=chunk, name="ragged-seq")
+    note(f"prefill ragged sequential carry dtype={dtype} chunk={chunk} dk={dk} dv={dv}")
+    y = conv_inputs(orc, inp)
+    o, S = _run_gpu(G, inp, y, state0=inp.state0)
+    o_ref, S_ref = _oracle(orc, inp, y)
+    eo, es = _compare(inp, o, S, o_ref, S_ref)
+    note(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype,dk,dv,tiled,l2,scale", [
     ("f32", 64, 128, True, True, 0.0883883), ("bf16", 128, 64, False, True, 1.0),
     ("f32", 64, 64, False, False, 1.0), ("bf16", 64, 128, True, True, 0.5)])
