@@ -127,7 +127,7 @@ int64_t max_segs(const gdn_dims* d) {
 
 // Workspace: [chunk table (varlen only)] [Tt, P per chunk and v-head]
 // [a, b, c, e^{gamma_last} per chunk and v-head], and on the segment path
-// [segment table (varlen only)] [segment start states, fp32]
+// [segment table and dispatch order (varlen only)] [segment start states, fp32]
 // [segment transitions, bf16]; each part 256-byte aligned.
 struct WsLayout {
   size_t table_off, table_bytes, mats_off, mats_bytes, scal_off, scal_bytes;
@@ -150,7 +150,8 @@ WsLayout ws_layout(const gdn_dims* d) {
   w.segt_bytes = w.sst_bytes = w.phi_bytes = 0;
   if (seg_enabled(d)) {
     const size_t segs = (size_t)max_segs(d) * d->num_v_heads;
-    w.segt_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1) * 4);
+    // varlen: segment offsets [num_seqs + 1], then the dispatch order [max_segs]
+    w.segt_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1 + max_segs(d)) * 4);
     w.sst_bytes = align256(segs * d->head_dim_k * d->head_dim_v * 4);
     w.phi_bytes = align256(segs * d->head_dim_k * d->head_dim_k * 2);
   }
@@ -280,6 +281,7 @@ void carve(gdn::ScanArgs& a, const gdn_dims* d, const void* ws) {
     a.seg_len = seg_len(d);
     a.max_segs = (int)max_segs(d);
     a.seg_offsets = L.segt_bytes ? reinterpret_cast<int32_t*>(base + L.segt_off) : nullptr;
+    a.seg_perm = a.seg_offsets ? a.seg_offsets + (d->num_seqs + 1) : nullptr;
     a.seg_state = base ? reinterpret_cast<float*>(base + L.sst_off) : nullptr;
     a.seg_phi = base ? reinterpret_cast<uint16_t*>(base + L.phi_off) : nullptr;
   }

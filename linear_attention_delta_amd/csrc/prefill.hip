@@ -84,6 +84,40 @@ __global__ void __launch_bounds__(1024) k_chunk_table(ScanArgs a) {
     a.chunk_offsets[0] = 0;
     if (a.seg_offsets) a.seg_offsets[0] = 0;
   }
+  // The segment path's dispatch order: segments by chunk count, longest
+  // first (ties by index), so the longest chains start in the first round
+  // of workgroups.  A rank sort, one segment per thread, up to 1024
+  // segments; past that the identity.  Only the order changes, not what any
+  // workgroup computes.
+  if (a.seg_perm) {
+    __shared__ int slen[1024];
+    const int total = carry[1];
+    if (total <= 1024) {
+      // then num_seqs <= 1024 (a sequence has at least one segment): the loop
+      // above ran once, and buf[1][i] is sequence i's inclusive segment count
+      const int i = threadIdx.x;
+      if (i < a.num_seqs) {
+        const int len = a.cu_seqlens[i + 1] - a.cu_seqlens[i];
+        const int n = (len + a.chunk - 1) / a.chunk;
+        const int ns = n > 0 ? (n + a.seg_len - 1) / a.seg_len : 1;
+        const int first = buf[1][i] - ns;
+        for (int p = 0; p < ns; p++) slen[first + p] = min(a.seg_len, n - p * a.seg_len);  // 0: empty sequence
+      }
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < total) {
+        const int lt = slen[t];
+        int rank = 0;
+        for (int u = 0; u < total; u++) {
+          const int lu = slen[u];
+          rank += (lu > lt) || (lu == lt && u < t);
+        }
+        a.seg_perm[rank] = t;
+      }
+    } else {
+      for (int t = threadIdx.x; t < total; t += 1024) a.seg_perm[t] = t;
+    }
+  }
 }
 
 // Locate global chunk n: its sequence, first token and length.  false if

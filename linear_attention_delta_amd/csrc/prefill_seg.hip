@@ -79,7 +79,9 @@ __device__ __forceinline__ Seg seg_of(const ScanArgs& a, int C, int n) {
 
 // Block -> (global segment, v-head).  The G v-heads reading one q/k head in
 // one segment get the same blockIdx % 8, i.e. the same XCD, and share its L2
-// for K and Q.
+// for K and Q.  With variable lengths the segments are taken in the order
+// the chunk table chose (longest first): the passes hold one workgroup per
+// compute unit, so a long chain dispatched late would set the end time.
 __device__ __forceinline__ void block_unit(const ScanArgs& a, int& n, int& hk, int& h) {
   const int G = a.hv / a.hk;
   const int xcd = blockIdx.x & 7, m8 = blockIdx.x >> 3;
@@ -88,6 +90,7 @@ __device__ __forceinline__ void block_unit(const ScanArgs& a, int& n, int& hk, i
   n = grp / a.hk;
   hk = grp % a.hk;
   h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
+  if (a.seg_perm && n < a.seg_offsets[a.num_seqs]) n = a.seg_perm[n];
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) { return (uint16_t)(cvt_bf16x2(x, 0.f) & 0xffffu); }

@@ -112,12 +112,14 @@ def test_workspace_size(g):
     d = _dims(g, chunk_size=16)
     units = 256 * 32
     assert g.workspace_size(d) == a256(units * 2 * 16 * 16 * 2) + a256(units * 8 * 16 * 4)
-    # varlen: chunk table + upper bound of chunks; segments bounded by chunks / 8 + sequences
+    # varlen: chunk table + upper bound of chunks; segments bounded by chunks / 8 + sequences; the
+    # segment table holds the offsets [sequences + 1] and the dispatch order [segments]
     d = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5)
     chunks = 1000 // 64 + 5
     units = chunks * 32
+    segs = chunks // 8 + 5
     assert g.workspace_size(d) == (256 + a256(units * 2 * 64 * 64 * 2) + a256(units * 8 * 64 * 4)
-                                   + seg_parts(chunks // 8 + 5, table=256))
+                                   + seg_parts(segs, table=a256((5 + 1 + segs) * 4)))
     assert g.lib.gdn_prefill_workspace_size(ctypes.byref(_dims(g, chunk_size=8))) == 0
 
 
