@@ -167,6 +167,23 @@ def test_multi_segment_bf16(G, orc, chunk, dk, dv, tiled, lens):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("nseq", [1000, 1100])
+def test_many_segments_bf16(G, orc, nseq):
+    """Many short sequences on the segment path: the passes take up to 1024
+    segments longest first and more in index order (1000 and 1100 segments,
+    lengths 0..150 with empty ones among them)."""
+    sh = synth.LayerShape(1, 2, 64, 64)
+    lens = [int(x) for x in np.random.default_rng(nseq).integers(0, 151, size=nseq)]
+    inp = synth.make_prefill(nseq, sh, lens, "bf16", state0_std=0.05, chunk_size=64, name="many-seg")
+    note(f"prefill many segments nseq={nseq} tokens={sum(lens)}")
+    y = conv_inputs(orc, inp)
+    o, S = _run_gpu(G, inp, y, state0=inp.state0)
+    o_ref, S_ref = _oracle(orc, inp, y)
+    eo, es = _compare(inp, o, S, o_ref, S_ref)
+    note(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_qwen35_4k_bf16(G, orc):
     """B=1, T=4096, 16/32 heads, d=128, bf16, chunk 64 -- the benchmark's
     launch configuration; every v-head against the oracle."""
