@@ -184,8 +184,9 @@ gdn_status gdn_conv1d(int32_t num_seqs, int32_t total_tokens, int32_t seqlen,
  * Tt and room for the score matrix P (both C x C in the q/k/v dtype) and
  * eight C-vectors of fp32 per-token factors, plus the chunk table for varlen
  * input; for bf16 with chunk 32 or 64 also, per carry segment and v-head,
- * an fp32 start state and a bf16 d_k x d_k transition (and a segment table
- * for varlen input).  0 on invalid dims (gdn_last_error says why).
+ * an fp32 start state and a bf16 d_k x d_k transition (and, for varlen
+ * input, a segment table with the order in which the carry takes the
+ * segments).  0 on invalid dims (gdn_last_error says why).
  */
 size_t gdn_prefill_workspace_size(const gdn_dims *d);
 
@@ -240,10 +241,11 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_dims *d, const void *q, const v
  * all state-independent work in batch).  For every chunk and v-head it
  * writes into the workspace Tt = (I + A)^{-1} diag(beta), the causal score
  * matrix P[r][s] = e^{gamma_r - gamma_s} q_hat_r . k_hat_s (s <= r) and the
- * per-token scale factors; fully parallel over chunks.  For bf16 with chunk
- * 32 or 64 the carry forms P itself from q and k, so P is not written and
- * Tt is kept as its nonzero (lower) 16x16 blocks only.  The workspace
- * layout is private to the library.  Arguments as gdn_prefill_chunked.
+ * per-token scale factors; fully parallel over chunks.  Tt and P are kept
+ * as their nonzero (lower) 16x16 blocks only.  For bf16 with chunk 32 or 64
+ * the carry forms P itself from q and k, so P is not written.  The
+ * workspace layout is private to the library.  Arguments as
+ * gdn_prefill_chunked.
  */
 gdn_status gdn_prefill_prepare(const gdn_dims *d, const void *q, const void *k,
                                const float *g, const float *beta,
