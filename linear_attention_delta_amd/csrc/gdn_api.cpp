@@ -141,7 +141,9 @@ WsLayout ws_layout(const gdn_dims* d) {
   const size_t units = (size_t)max_chunks(d) * d->num_v_heads;
   const size_t C = d->chunk_size;
   w.table_off = 0;
-  w.table_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1) * 4);
+  // varlen: chunk offsets [num_seqs + 1], and on the sequential carry its
+  // dispatch order [num_seqs] (the segment path keeps its own below)
+  w.table_bytes = d->seqlen > 0 ? 0 : align256((size_t)(d->num_seqs + 1 + (seg_enabled(d) ? 0 : d->num_seqs)) * 4);
   w.mats_off = w.table_bytes;
   w.mats_bytes = align256(units * 2 * C * C * elem_size(d->dtype));
   w.scal_off = w.mats_off + w.mats_bytes;
@@ -284,6 +286,8 @@ void carve(gdn::ScanArgs& a, const gdn_dims* d, const void* ws) {
     a.seg_perm = a.seg_offsets ? a.seg_offsets + (d->num_seqs + 1) : nullptr;
     a.seg_state = base ? reinterpret_cast<float*>(base + L.sst_off) : nullptr;
     a.seg_phi = base ? reinterpret_cast<uint16_t*>(base + L.phi_off) : nullptr;
+  } else if (a.chunk_offsets) {
+    a.seg_perm = a.chunk_offsets + (d->num_seqs + 1);
   }
 }
 

@@ -58,7 +58,8 @@ struct ScanArgs {
   int seg_len;
   int max_segs;               // bound on the number of segments, all sequences
   int32_t* seg_offsets;       // [num_seqs + 1], varlen only
-  int32_t* seg_perm;          // [max_segs], varlen only: global segments in the order the passes take them
+  int32_t* seg_perm;          // varlen only: the carry's units (segments, or sequences on the sequential
+                              // carry) in the order its workgroups take them, longest first
   float* seg_state;           // [max_segs][hv][dk][dv] fp32: start state of each segment
   uint16_t* seg_phi;          // [max_segs][hv][dk][dk] bf16: transition of each segment
   // decode only

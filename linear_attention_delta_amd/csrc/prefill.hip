@@ -84,14 +84,15 @@ __global__ void __launch_bounds__(1024) k_chunk_table(ScanArgs a) {
     a.chunk_offsets[0] = 0;
     if (a.seg_offsets) a.seg_offsets[0] = 0;
   }
-  // The segment path's dispatch order: segments by chunk count, longest
-  // first (ties by index), so the longest chains start in the first round
-  // of workgroups.  A rank sort, one segment per thread, up to 1024
-  // segments; past that the identity.  Only the order changes, not what any
-  // workgroup computes.
+  // The carry's dispatch order: its units (segments on the segment path,
+  // else sequences) by chunk count, longest first (ties by index), so the
+  // longest chains start in the first round of workgroups.  A rank sort,
+  // one unit per thread, up to 1024 units; past that the identity.  Only
+  // the order changes, not what any workgroup computes.
   if (a.seg_perm) {
     __shared__ int slen[1024];
-    const int total = carry[1];
+    const bool segs = a.seg_offsets != nullptr;
+    const int total = segs ? carry[1] : a.num_seqs;
     if (total <= 1024) {
       // then num_seqs <= 1024 (a sequence has at least one segment): the loop
       // above ran once, and buf[1][i] is sequence i's inclusive segment count
@@ -99,9 +100,13 @@ __global__ void __launch_bounds__(1024) k_chunk_table(ScanArgs a) {
       if (i < a.num_seqs) {
         const int len = a.cu_seqlens[i + 1] - a.cu_seqlens[i];
         const int n = (len + a.chunk - 1) / a.chunk;
-        const int ns = n > 0 ? (n + a.seg_len - 1) / a.seg_len : 1;
-        const int first = buf[1][i] - ns;
-        for (int p = 0; p < ns; p++) slen[first + p] = min(a.seg_len, n - p * a.seg_len);  // 0: empty sequence
+        if (segs) {
+          const int ns = n > 0 ? (n + a.seg_len - 1) / a.seg_len : 1;
+          const int first = buf[1][i] - ns;
+          for (int p = 0; p < ns; p++) slen[first + p] = min(a.seg_len, n - p * a.seg_len);  // 0: empty sequence
+        } else {
+          slen[i] = n;
+        }
       }
       __syncthreads();
       const int t = threadIdx.x;
@@ -728,7 +733,9 @@ __global__ void __launch_bounds__(256 * NT * (SPLIT ? 2 : 1)) k_scan(ScanArgs a)
   const int grp = (m / GS) * 8 + xcd;
   if (grp >= ngroups) return;
   const int local = m % GS;
-  const int seq = grp / a.hk, hk = grp % a.hk;
+  const int hk = grp % a.hk;
+  // with variable lengths, sequences in the chunk table's order (longest first)
+  const int seq = a.seg_perm ? a.seg_perm[grp / a.hk] : grp / a.hk;
   const int vh = local / nblk;
   const int h = a.tiled ? (hk + vh * a.hk) : (hk * G + vh);
   const int dv0 = (local % nblk) * 16 * NT;

@@ -112,6 +112,11 @@ def test_workspace_size(g):
     d = _dims(g, chunk_size=16)
     units = 256 * 32
     assert g.workspace_size(d) == a256(units * 2 * 16 * 16 * 2) + a256(units * 8 * 16 * 4)
+    # varlen on the sequential carry: the chunk table holds the offsets [sequences + 1] and the
+    # order in which the carry takes the sequences [sequences]
+    d = _dims(g, dtype=g.GDN_F32, seqlen=0, total_tokens=5000, num_seqs=70)
+    units = (5000 // 64 + 70) * 32
+    assert g.workspace_size(d) == a256((70 + 1 + 70) * 4) + a256(units * 2 * 64 * 64 * 4) + a256(units * 8 * 64 * 4)
     # varlen: chunk table + upper bound of chunks; segments bounded by chunks / 8 + sequences; the
     # segment table holds the offsets [sequences + 1] and the dispatch order [segments]
     d = _dims(g, seqlen=0, total_tokens=1000, num_seqs=5)
